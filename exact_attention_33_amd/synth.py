@@ -1,0 +1,71 @@
+"""Seeded synthetic workloads for the attention hot path.
+
+Shared by the tests and the benchmark; it holds shapes, seeds and random draws
+only -- none of the attention arithmetic -- so neither the oracle nor the HIP
+library depends on the other through it.
+
+Recipe: per workload, one ``torch.Generator`` on the target device seeded with
+the workload's seed (0..4 in the order listed below); ``q``, then ``k``, then
+``v`` are drawn i.i.d. N(0, 1) in fp32 and rounded to the workload dtype
+(round-to-nearest-even, torch's ``.to``).  ``scale = 1/sqrt(D)``.
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+# name -> shape and mask of each workload; the seed is its position.
+WORKLOADS = {
+    "tiny_f32": dict(kind="prefill", B=1, Hq=1, Hkv=1, Sq=128, Sk=128, D=64,
+                     dtype="f32", causal=0, window=-1),
+    "causal_prefill": dict(kind="prefill", B=4, Hq=16, Hkv=16, Sq=2048, Sk=2048, D=128,
+                           dtype="bf16", causal=1, window=-1),
+    "window_encoder": dict(kind="prefill", B=8, Hq=12, Hkv=12, Sq=8192, Sk=8192, D=64,
+                           dtype="bf16", causal=0, window=64),
+    "gqa_decode": dict(kind="decode", B=16, Hq=32, Hkv=8, Sk=32768, D=128,
+                       dtype="bf16", num_splits=64),
+    "long_decode": dict(kind="decode", B=1, Hq=32, Hkv=8, Sk=1048576, D=128,
+                        dtype="bf16", num_splits=256),
+}
+SEEDS = {name: i for i, name in enumerate(WORKLOADS)}
+
+TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)
+
+
+def draw_qkv(q_shape, kv_shape, dtype: str, seed: int, device="cpu"):
+    """Draw q, k, v ~ N(0,1) in fp32 from one seeded generator, then round to ``dtype``."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    td = TORCH_DTYPES[dtype]
+    q = torch.randn(q_shape, generator=gen, device=device, dtype=torch.float32).to(td)
+    k = torch.randn(kv_shape, generator=gen, device=device, dtype=torch.float32).to(td)
+    v = torch.randn(kv_shape, generator=gen, device=device, dtype=torch.float32).to(td)
+    return q, k, v
+
+
+def workload_inputs(name: str, device="cpu", seed: int | None = None):
+    """Inputs of a named workload: dict with q, k, v and the call parameters."""
+    w = dict(WORKLOADS[name])
+    s = SEEDS[name] if seed is None else seed
+    if w["kind"] == "prefill":
+        qs = (w["B"], w["Hq"], w["Sq"], w["D"])
+    else:
+        qs = (w["B"], w["Hq"], w["D"])
+    kvs = (w["B"], w["Hkv"], w["Sk"], w["D"])
+    q, k, v = draw_qkv(qs, kvs, w["dtype"], s, device)
+    w.update(q=q, k=k, v=v, scale=default_scale(w["D"]), seed=s, name=name)
+    return w
+
+
+def to_numpy_exact(t: torch.Tensor):
+    """Host copy whose values equal the tensor's bit-exactly (bf16 widens to fp32)."""
+    t = t.detach().to("cpu")
+    if t.dtype == torch.bfloat16:
+        t = t.to(torch.float32)
+    return t.numpy()
