@@ -1,0 +1,226 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one causal prefill (B=4, H=16, S=2048, D=128, bf16) followed by one
+split-KV GQA decode (B=16, Hq=32, Hkv=8, Sk=32768, D=128, 64 splits, bf16):
+the prefill kernel plus the decode split and tree-combine kernels.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Prints ONE JSON line.  `value` is the mean of the two roofline fractions, in
+percent: prefill TFLOP/s over the dense bf16 MFMA peak and decode KV GB/s over
+the HBM peak.  Per-call durations come from HIP events recorded on the stream
+the kernels are launched on, inside the timed region.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+
+PREFILL = "causal_prefill"
+DECODE = "gqa_decode"
+KERNEL_SOURCES = ["fwd_bf16.hip", "decode.hip", "common.h"]
+
+
+def visible_pairs_causal(Sq: int, Sk: int) -> int:
+    """Number of (query, key) pairs a bottom-right causal mask keeps."""
+    off = Sk - Sq
+    return sum(max(0, min(Sk, i + off + 1)) for i in range(Sq))
+
+
+def prefill_flops(w) -> float:
+    pairs = visible_pairs_causal(w["Sq"], w["Sk"])
+    return 4.0 * w["D"] * pairs * w["B"] * w["Hq"]
+
+
+def decode_kv_bytes(w) -> float:
+    return 2.0 * w["B"] * w["Hkv"] * w["Sk"] * w["D"] * 2
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_attention_33_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kind: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    entry = rec.get(kind)
+    if not entry or entry.get("source_digest") != source_digest():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(budget_s: float = 20.0):
+    """The fp64 oracle, untuned, on a bounded sample of the same workloads."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from exact_attention_33_amd import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info()]
+        threads = max([n for _, n in blas if n] or [1])
+    except Exception:  # noqa: BLE001
+        blas, threads = [], 1
+    wp = synth.WORKLOADS[PREFILL]
+    wd = synth.WORKLOADS[DECODE]
+    scale_p = synth.default_scale(wp["D"])
+    # prefill sample: (b, h) heads of the causal workload, one at a time, until
+    # half the budget is spent or all 64 are done
+    nh, tp = 0, 0.0
+    while tp < budget_s / 2 and nh < wp["B"] * wp["Hq"]:
+        q, k, v = synth.draw_qkv((1, 1, wp["Sq"], wp["D"]), (1, 1, wp["Sk"], wp["D"]), "bf16", 100 + nh)
+        qn, kn, vn = (synth.to_numpy_exact(t) for t in (q, k, v))
+        t0 = time.perf_counter()
+        oracle.attention(qn, kn, vn, scale_p, True)
+        tp += time.perf_counter() - t0
+        nh += 1
+    flops = 4.0 * wp["D"] * visible_pairs_causal(wp["Sq"], wp["Sk"]) * nh
+    # decode sample: batch rows of the GQA decode workload, same rule
+    nb, td, kv_bytes = 0, 0.0, 0.0
+    while td < budget_s / 2 and nb < wd["B"]:
+        q, k, v = synth.draw_qkv((1, wd["Hq"], wd["D"]), (1, wd["Hkv"], wd["Sk"], wd["D"]), "bf16", 200 + nb)
+        qn, kn, vn = (synth.to_numpy_exact(t) for t in (q, k, v))
+        t0 = time.perf_counter()
+        oracle.decode(qn, kn, vn, synth.default_scale(wd["D"]))
+        td += time.perf_counter() - t0
+        kv_bytes += 2.0 * wd["Hkv"] * wd["Sk"] * wd["D"] * 2
+        nb += 1
+    tflops = flops / tp / 1e12
+    gbs = kv_bytes / td / 1e9
+    value = 100.0 * 0.5 * (tflops / PEAK_BF16_TFLOPS + gbs / PEAK_HBM_GBS)
+    del np, torch
+    return {
+        "value": value, "unit": "% of MI355X peak (mean of prefill MFMA and decode HBM fractions)",
+        "cores": threads, "kind": "oracle",
+        "sample": (f"fp64 numpy oracle, timed per call: causal prefill on {nh} of 64 heads (S=2048, D=128) took "
+                   f"{tp:.2f} s -> {tflops * 1e3:.2f} GFLOP/s; decode on {nb} of 16 batch rows "
+                   f"(Hq=32, Hkv=8, Sk=32768) took {td:.2f} s -> {gbs:.2f} GB/s of bf16 KV"),
+        "prefill_gflops": tflops * 1e3, "decode_gbs": gbs,
+        "affinity_cores": len(os.sched_getaffinity(0)), "blas": blas,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from exact_attention_33_amd import ops, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wp = synth.workload_inputs(PREFILL, dev)
+    wd = synth.workload_inputs(DECODE, dev)
+    o_p = torch.empty_like(wp["q"])
+    lse_p = torch.empty(wp["B"], wp["Hq"], wp["Sq"], dtype=torch.float32, device=dev)
+    o_d = torch.empty_like(wd["q"])
+    lse_d = torch.empty(wd["B"], wd["Hq"], dtype=torch.float32, device=dev)
+    ws = torch.empty(ops.decode_workspace_bytes(wd["B"], wd["Hq"], wd["D"], wd["num_splits"]),
+                     dtype=torch.uint8, device=dev)
+
+    def prefill():
+        ops.attn_fwd(wp["q"], wp["k"], wp["v"], causal=True, scale=wp["scale"], out=o_p, lse=lse_p)
+
+    def decode():
+        ops.attn_decode_ex(wd["q"], wd["k"], wd["v"], wd["num_splits"], scale=wd["scale"], out=o_d,
+                           lse=lse_d, workspace=ws)
+
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        prefill()
+        ev[i][1].record(stream)
+        decode()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    p_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    d_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    step_ms = ev[0][0].elapsed_time(ev[-1][2]) / args.steps
+    p_avg = sum(p_ms) / len(p_ms)
+    d_avg = sum(d_ms) / len(d_ms)
+
+    flops = prefill_flops(wp)
+    kv = decode_kv_bytes(wd)
+    p_tflops = flops / (p_avg * 1e-3) / 1e12
+    d_gbs = kv / (d_avg * 1e-3) / 1e9
+    p_frac = p_tflops / PEAK_BF16_TFLOPS
+    d_frac = d_gbs / PEAK_HBM_GBS
+    value = 100.0 * 0.5 * (p_frac + d_frac)
+
+    line = {
+        "metric": "prefill attn TFLOP/s + decode KV GB/s, as % of MI355X MFMA/HBM peak",
+        "value": round(value, 3),
+        "unit": "% of MI355X peak (mean of prefill MFMA and decode HBM fractions)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {
+            "workload": ("causal prefill B4 H16 S2048 D128 bf16 + GQA decode B16 Hq32 Hkv8 "
+                         "Sk32768 D128 bf16, 64 KV splits"),
+            "prefill": {k: wp[k] for k in ("B", "Hq", "Hkv", "Sq", "Sk", "D", "causal", "window")},
+            "decode": {k: wd[k] for k in ("B", "Hq", "Hkv", "Sk", "D", "num_splits")},
+        },
+        "roofline": {
+            "kernel": "decode (split kernel + tree combine), the larger share of the step",
+            "bound": "hbm", "achieved": round(d_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(d_frac, 4), "traffic": measured_traffic("decode"),
+            "algorithmic_bytes": kv, "avg_launch_ms": round(d_avg, 5),
+        },
+        "roofline_prefill": {
+            "kernel": "fwd_bf16 causal prefill",
+            "bound": "mfma", "achieved": round(p_tflops, 1), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(p_frac, 4), "traffic": measured_traffic("prefill"),
+            "algorithmic_flops": flops, "avg_launch_ms": round(p_avg, 5),
+        },
+        "wall_s_timed": round(wall, 4),
+        "kernel_source_digest": source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

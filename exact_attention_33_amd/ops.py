@@ -1,0 +1,179 @@
+"""ctypes binding of libattn.so: same entry points as include/attn.h.
+
+Argument marshalling only -- tensor checks, output allocation, device pointers
+and torch's current HIP stream.  Every step of the computation runs in the
+HIP kernels behind the C ABI.  If the library is not built the first call
+raises; there is no CPU fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+ATTN_OK = 0
+STATUS_NAMES = {
+    0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_GQA",
+    4: "ATTN_ERR_HEADDIM", 5: "ATTN_ERR_SPLITS", 6: "ATTN_ERR_WINDOW",
+    7: "ATTN_ERR_WORKSPACE", 8: "ATTN_ERR_HIP", 9: "ATTN_ERR_ARG",
+}
+# every symbol include/attn.h declares
+EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_decode", "attn_decode_ex",
+           "attn_decode_workspace_bytes", "attn_error_string", "attn_version")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libattn.so once and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m exact_attention_33_amd.build` "
+                           "(there is no CPU fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
+    L.attn_fwd.restype = i
+    L.attn_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
+    L.attn_fwd_f32.restype = i
+    L.attn_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    L.attn_decode.restype = i
+    L.attn_decode_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    L.attn_decode_ex.restype = i
+    L.attn_decode_workspace_bytes.argtypes = [i, i, i, i]
+    L.attn_decode_workspace_bytes.restype = sz
+    L.attn_error_string.argtypes = [i]
+    L.attn_error_string.restype = ctypes.c_char_p
+    L.attn_version.argtypes = []
+    L.attn_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def error_string(status: int) -> str:
+    return lib().attn_error_string(int(status)).decode()
+
+
+def version() -> str:
+    return lib().attn_version().decode()
+
+
+def decode_workspace_bytes(B: int, Hq: int, D: int, num_splits: int) -> int:
+    return int(lib().attn_decode_workspace_bytes(B, Hq, D, num_splits))
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        raise AttnError(status, error_string(status))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _want(t: torch.Tensor, name: str, dtype, ndim: int, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype or t.dim() != ndim or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name}: need a contiguous {dtype} tensor with {ndim} dims on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def _fwd(fn, dtype, q, k, v, causal, window, scale, out, lse, return_lse):
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be on a GPU")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _want(t, n, dtype, 4, dev)
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, Sk, Dk = k.shape
+    if v.shape != k.shape or Bk != B or Dk != D:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    o = torch.empty_like(q) if out is None else out
+    _want(o, "out", dtype, 4, dev)
+    if o.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _want(lse, "lse", torch.float32, 3, dev)
+        if tuple(lse.shape) != (B, Hq, Sq):
+            raise ValueError("lse must be [B, Hq, Sq]")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Sk, D,
+              int(causal), int(window), scale, _stream(q)))
+    return o, lse
+
+
+def attn_fwd(q, k, v, causal=False, window=-1, scale=None, out=None, lse=None, return_lse=True):
+    """Prefill, bf16 ``q [B,Hq,Sq,D]``, ``k, v [B,Hkv,Sk,D]`` -> ``(o, lse)``."""
+    return _fwd(lib().attn_fwd, torch.bfloat16, q, k, v, causal, window, scale, out, lse, return_lse)
+
+
+def attn_fwd_f32(q, k, v, causal=False, window=-1, scale=None, out=None, lse=None, return_lse=True):
+    """Prefill on fp32 tensors (no bf16 rounding anywhere) -> ``(o, lse)``."""
+    return _fwd(lib().attn_fwd_f32, torch.float32, q, k, v, causal, window, scale, out, lse, return_lse)
+
+
+def _decode_shapes(q, kcache, vcache, out):
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be on a GPU")
+    _want(q, "q", torch.bfloat16, 3, dev)
+    _want(kcache, "kcache", torch.bfloat16, 4, dev)
+    _want(vcache, "vcache", torch.bfloat16, 4, dev)
+    B, Hq, D = q.shape
+    Bk, Hkv, Sk, Dk = kcache.shape
+    if vcache.shape != kcache.shape or Bk != B or Dk != D:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(kcache.shape)} v{tuple(vcache.shape)}")
+    o = torch.empty_like(q) if out is None else out
+    _want(o, "out", torch.bfloat16, 3, dev)
+    if o.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    return B, Hq, Hkv, Sk, D, o
+
+
+def attn_decode(q, kcache, vcache, num_splits, out=None):
+    """Split-KV decode with the library workspace, scale 1/sqrt(D) -> ``o [B,Hq,D]``."""
+    B, Hq, Hkv, Sk, D, o = _decode_shapes(q, kcache, vcache, out)
+    _check(lib().attn_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(o), B, Hq, Hkv, Sk, D,
+                             int(num_splits), _stream(q)))
+    return o
+
+
+def attn_decode_ex(q, kcache, vcache, num_splits, scale=None, out=None, lse=None,
+                   return_lse=True, workspace=None):
+    """Split-KV decode with explicit scale and caller workspace -> ``(o, lse)``.
+
+    ``workspace`` (a uint8 device tensor) is allocated here when not given.
+    """
+    B, Hq, Hkv, Sk, D, o = _decode_shapes(q, kcache, vcache, out)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _want(lse, "lse", torch.float32, 2, q.device)
+    need = decode_workspace_bytes(B, Hq, D, int(num_splits)) if num_splits >= 1 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib().attn_decode_ex(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(o), _ptr(lse), B, Hq, Hkv,
+                                Sk, D, int(num_splits), scale, _ptr(workspace), workspace.numel(),
+                                _stream(q)))
+    return o, lse

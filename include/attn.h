@@ -1,0 +1,131 @@
+/*
+ * attn.h -- exact softmax attention on AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * What is computed (all entry points): for every batch b, query head h and
+ * query row i,
+ *
+ *     s_ij   = scale * <q[b,h,i,:], k[b,g,j,:]>          g = h / (Hq / Hkv)
+ *     lse_i  = ln( sum_{j visible} exp(s_ij) )
+ *     o_i    = sum_{j visible} exp(s_ij - lse_i) * v[b,g,j,:]
+ *
+ * i.e. standard attention; the FlashAttention explainer (aiunderstanding.org,
+ * "Deep dive" and FAQ) states the tiled fused method returns exactly these
+ * values while never writing the score matrix to memory, which is what the
+ * kernels behind this header do.  The split-KV decode merges per-chunk
+ * partials with the log-sum-exp operator in a tree along the sequence axis
+ * (Tree Attention abstract, express24.ir page).
+ *
+ * Visibility of key j to query i, with c = i + (Sk - Sq) (bottom-right
+ * alignment):  [causal == 0 || j <= c]  &&  [window < 0 || |c - j| <= window].
+ * A sliding window is local attention -- each token attends only to its
+ * neighbours (thread on extending LLM context, point 1).  A row with no
+ * visible key gets o = 0 and lse = -inf.
+ *
+ * Layout: every tensor is dense, row-major, last dimension fastest:
+ *     q, o   [B, Hq,  Sq, D]     (decode: [B, Hq, D])
+ *     k, v   [B, Hkv, Sk, D]     (decode: the KV cache, same shape)
+ *     lse    [B, Hq,  Sq] fp32   (decode: [B, Hq])
+ * Device pointers only (memory from hipMalloc or a framework allocator on the
+ * current device).  The caller owns every buffer; the library never frees or
+ * keeps a caller pointer after the call returns.
+ *
+ * Execution: every call only enqueues work on `stream` (NULL = the default
+ * stream) and returns; there is no host synchronisation.  Arguments are
+ * checked on the host first; on any error nothing is enqueued and nothing is
+ * written.  No C++ exception crosses this boundary.  Return value: ATTN_OK or
+ * one of the codes below; attn_error_string() names it.
+ */
+#ifndef EXACT_ATTENTION_ATTN_H
+#define EXACT_ATTENTION_ATTN_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,      /* a required pointer is NULL                                  */
+  ATTN_ERR_SHAPE = 2,     /* a size is negative, or too large for the kernels' indexing  */
+  ATTN_ERR_GQA = 3,       /* Hkv < 1 while Hq > 0, or Hq % Hkv != 0                      */
+  ATTN_ERR_HEADDIM = 4,   /* D is not 64 or 128                                          */
+  ATTN_ERR_SPLITS = 5,    /* num_splits < 1, or num_splits > max(Sk, 1)                  */
+  ATTN_ERR_WINDOW = 6,    /* window < -1                                                 */
+  ATTN_ERR_WORKSPACE = 7, /* workspace NULL or smaller than attn_decode_workspace_bytes */
+  ATTN_ERR_HIP = 8,       /* the HIP runtime reported an error (launch, allocation)      */
+  ATTN_ERR_ARG = 9        /* causal not 0/1, or scale not finite and > 0                 */
+} attn_status;
+
+/*
+ * Prefill forward pass, bf16 q/k/v/o, fp32 accumulation and softmax.
+ *
+ *   q, k, v, o : bf16 device tensors in the layout above (k, v may be NULL
+ *                when Sk == 0; nothing is read or written when B*Hq*Sq == 0).
+ *   lse        : fp32 [B, Hq, Sq], or NULL to skip it.
+ *   causal     : 0 or 1.   window: -1 for none, else the half width w >= 0.
+ *   scale      : finite, > 0 (usually 1/sqrt(D)).
+ *   D          : 64 or 128.   Hq % Hkv == 0.
+ * o is rounded once, round-to-nearest-even, from fp32.  One kernel launch;
+ * the Sq x Sk score matrix never leaves the chip.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int Sq, int Sk, int D,
+             int causal, int window, float scale, hipStream_t stream);
+
+/*
+ * The same computation for fp32 q/k/v/o; arithmetic stays in fp32 (nothing
+ * is rounded to bf16).  Same arguments and errors as attn_fwd.
+ */
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                 int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                 int causal, int window, float scale, hipStream_t stream);
+
+/*
+ * Single-token decode against a KV cache, bf16, scale = 1/sqrt(D), split-KV.
+ *
+ *   q, o           : bf16 [B, Hq, D].   kcache, vcache: bf16 [B, Hkv, Sk, D].
+ *   num_splits     : 1 <= num_splits <= max(Sk, 1).  Chunk c covers keys
+ *                    [c*L, min((c+1)*L, Sk)), L = ceil(Sk / num_splits); an
+ *                    empty chunk is the merge identity.
+ * Two launches on `stream`: the split kernel writes one (m, l, acc) partial
+ * per (b, h, chunk); the combine kernel merges them with the log-sum-exp
+ * operator along a balanced binary tree over the chunk index and writes o.
+ * Uses a library-owned workspace per device that grows on demand (the first
+ * call at a new size allocates, which synchronises the device).  Calls that
+ * overlap in time on one device race on that workspace; use attn_decode_ex
+ * with a caller workspace for concurrent streams.
+ */
+int attn_decode(const void* q, const void* kcache, const void* vcache, void* o,
+                int B, int Hq, int Hkv, int Sk, int D, int num_splits, hipStream_t stream);
+
+/*
+ * attn_decode with an explicit scale, an optional lse output (fp32 [B, Hq],
+ * NULL to skip) and a caller-owned device workspace of at least
+ * attn_decode_workspace_bytes(B, Hq, D, num_splits) bytes.  Never allocates.
+ * The workspace contents on entry do not matter; it is scratch only.
+ */
+int attn_decode_ex(const void* q, const void* kcache, const void* vcache, void* o, float* lse,
+                   int B, int Hq, int Hkv, int Sk, int D, int num_splits, float scale,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Workspace bytes attn_decode_ex needs: one fp32 (m, l, acc[D]) partial per
+ * (b, h, chunk), B*Hq*num_splits*(D+2)*4, plus room for the upper tree levels
+ * when num_splits exceeds the 256 partials one combine workgroup merges.
+ * Returns 0 for invalid arguments.  Pure host function.
+ */
+size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits);
+
+/* Static, NUL-terminated name of a status code.  Pure host function. */
+const char* attn_error_string(int status);
+
+/* Library version string, e.g. "exact-attention gfx950 0.1".  Pure host function. */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_ATTN_H */
