@@ -3,33 +3,39 @@
 // registers only; nothing of size Sq x Sk ever reaches memory (FlashAttention
 // explainer, aiunderstanding.org, "Technical insight": blocks of q, k, v are
 // staged in on-chip memory, partial results are rescaled as each new block
-// arrives, and the whole computation is one fused kernel).
+// arrives, and the whole computation is one fused kernel).  Data movement is
+// overlapped with the matrix work and the softmax is interleaved with the
+// matrix products (the scheduling ideas of the FlashAttention-3 article,
+// ybx.com, "FA3 innovations"), here with gfx950 means.
 //
 // Work decomposition
 //   * one workgroup = 4 wavefronts = BM = 128 query rows of one (b, h);
-//     each wavefront owns 32 rows.  K and V tiles of BN keys are staged in
-//     LDS once per workgroup and read by all four wavefronts.
-//   * scores are computed transposed, S^T = K Q^T, with
-//     v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims (from LDS),
-//     B = 16 dims x 32 queries (Q fragment held in registers for the whole
-//     kernel).  In the accumulator each lane then holds ONE query (its lane
-//     mod 32) and 16 of the block's 32 keys, so the row max and row sum are
-//     mostly in-lane; one lane-swap (lane ^ 32) finishes the max.
-//   * the output is computed transposed too, O^T += V^T P^T: A = 32 dims x
-//     16 keys of V^T (LDS), B = the lane's own probabilities converted to
-//     bf16 -- no data movement between lanes.  This works because K rows are
-//     stored in LDS in a permuted order (bits 2 and 3 of the key index
-//     swapped within each 32-key block), which makes the 8 keys a lane holds
-//     for each 16-key step of the p v product contiguous.
-//   * V is stored in LDS transposed ([d][key]) so that the 8 keys an MFMA
-//     operand needs for one d are one 16-byte read; the transpose happens in
-//     registers while storing (pairs of bf16 from different keys are packed
-//     into one word).
-//   * LDS layouts are XOR-swizzled on 16-byte chunks so that both the
-//     cooperative stores and the MFMA operand reads are free of bank
-//     conflicts.
-//   * the next K/V tile is fetched from HBM into registers while the current
-//     one is being multiplied (register double buffering).
+//     each wavefront owns 32 rows.  Two workgroups share a CU.
+//   * K and V tiles of BN keys stream HBM -> LDS by buffer loads that write
+//     LDS directly (no register staging); out-of-range keys read as zero.
+//     K runs one tile ahead of V in two 2-slot rings, so while tile t is in
+//     its softmax, K(t+1) is already resident and K(t+2), V(t+1) are in
+//     flight.  One barrier per tile.
+//   * scores are computed transposed, S^T = K Q^T, on
+//     v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims from LDS, B = the Q
+//     fragment held in registers).  A lane then holds ONE query and 16 of a
+//     block's 32 keys: the row max is in-lane plus one lane^32 exchange, the
+//     row sum needs no exchange until the end.
+//   * the output is computed transposed too, O^T += V^T P^T: B = the lane's
+//     own probabilities in bf16 (no data movement between lanes), A = V^T read
+//     with the transposing LDS load ds_read_b64_tr_b16 from a row-major
+//     [key][dim] tile.  P lines up with V because K rows sit in LDS with bits
+//     2 and 3 of the key index swapped inside each 32-key block, which makes
+//     the 8 keys a lane holds for each 16-key step consecutive.
+//   * each wavefront issues the q k^T products of tile t+1 before the softmax
+//     of tile t, so the exponentials overlap matrix-core work.
+//   * the running max is only raised when a row's new maximum exceeds it by
+//     more than kSlack (base-2 units); otherwise probabilities are taken
+//     against the old reference (bounded by 2^kSlack), which skips most
+//     rescales of the accumulator.  The result is the same exact quantity.
+//   * LDS tiles are XOR-swizzled on 16-byte chunks (the buffer loads fetch
+//     the permuted source chunk per lane) so the MFMA operand reads are free
+//     of bank conflicts.
 //   * all softmax arithmetic is base 2: scores are multiplied by
 //     scale*log2(e) inside one FMA, exponentials use v_exp_f32.
 #include "common.h"
@@ -53,26 +59,38 @@ struct FwdArgs {
 
 constexpr int kBM = 128;
 constexpr int kThreads = 256;
+constexpr float kSlack = 8.0f;
 
-// Position in LDS of key row `r` of a tile: bits 2 and 3 swapped.
+// LDS row of key `r` of a K tile: bits 2 and 3 swapped (an involution).
 __device__ __forceinline__ int key_slot(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
+// 16-byte-chunk XOR swizzles of the K and V tiles (row = LDS row).
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+  if constexpr (D == 128) return row & 15;
+  else return ((row & 3) << 1) ^ ((row >> 2) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+  if constexpr (D == 128) return ((row & 3) << 2) + ((row >> 2) & 3);
+  else return ((row & 3) << 1) ^ ((row >> 2) & 7);
+}
+
 template <int D, int BN>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
-  constexpr int KCH = D / 8;                    // 16-byte chunks per row
-  constexpr int KLOADS = BN * KCH / kThreads;   // 16-byte loads per thread per K tile
-  constexpr int KPT = BN * KCH / kThreads;      // keys per thread in the V transpose
-  constexpr int VGRP = BN / KPT;                // key groups per V tile
-  constexpr int NKB = BN / 32;                  // 32-key blocks per tile
-  constexpr int NDB = D / 32;                   // 32-dim blocks of the output
-  constexpr int NQK = D / 16;                   // k-steps of q k^T
-  static_assert(KPT == 2 || KPT == 4, "V transpose packs 2 or 4 keys per thread");
-  static_assert(BN % 32 == 0 && BN / 8 >= 8, "V^T rows need >= 8 chunks for the swizzle");
+  constexpr int KCH = D / 8;                      // 16-byte chunks per row
+  constexpr int TILE = BN * D;                    // bf16 per K or V tile
+  constexpr int NBLK = TILE * 2 / 1024;           // 1 KB load blocks per tile
+  constexpr int BPW = NBLK / (kThreads / 64);     // blocks per wavefront
+  constexpr int NKB = BN / 32;                    // 32-key blocks per tile
+  constexpr int NDB = D / 32;                     // 32-dim blocks of the output
+  constexpr int NQK = D / 16;                     // k-steps of q k^T
+  static_assert(NBLK % 4 == 0, "tile must split into whole 1 KB blocks per wavefront");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[D * BN];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[2][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[2][TILE];
 
   // ---- which (b, h, query tile) this workgroup computes -----------------
   const int BH = a.B * a.Hq;
@@ -92,7 +110,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int b = bh / a.Hq, h = bh % a.Hq;
   const int g = h / (a.Hq / a.Hkv);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, l32 = lane & 31;
   const int off = a.Sk - a.Sq;
   const int w = a.window;
@@ -110,12 +129,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   const size_t q_base = ((size_t)b * a.Hq + h) * (size_t)a.Sq;
   const size_t kv_base = ((size_t)b * a.Hkv + g) * (size_t)a.Sk;
+  const uint16_t* kh = a.k + kv_base * D;
+  const uint16_t* vh = a.v + kv_base * D;
 
   const int qw0 = r0 + wave * 32;               // first row of this wavefront
   const int qw1 = min(qw0 + 31, a.Sq - 1);      // last valid row
   const int qi = qw0 + l32;                     // this lane's row
   const bool q_ok = qi < a.Sq;
   const bool wave_live = qw0 < a.Sq;
+  const int pos = qi + off;                     // key position aligned with the row
+  const int plo = qw0 + off, phi = qw1 + off;
 
   // ---- Q fragment (B operand of S^T = K Q^T) ----------------------------
   bf16x8 qf[NQK];
@@ -128,49 +151,57 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     }
   }
 
-  // ---- K/V tile fetch (HBM -> registers) and store (registers -> LDS) ----
-  u32x4 kr[KLOADS];
-  u32x4 vr[KPT];
-  const int vkg = tid % VGRP, vch = tid / VGRP;  // V: key group, 16-byte chunk
-
-  auto fetch = [&](int tile) {
+  // ---- tile loads: per-lane source offsets are the same for every tile ----
+  uint32_t koff[BPW], voff[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int p = (i * (kThreads / 64) + wave) * 64 + lane;  // 16-byte slot in the tile
+    const int row = p / KCH, pch = p % KCH;
+    koff[i] = (uint32_t)((key_slot(row) * D + (pch ^ swz_k<D>(row)) * 8) * 2);
+    voff[i] = (uint32_t)((row * D + (pch ^ swz_v<D>(row)) * 8) * 2);
+  }
+  const uint32_t sK0 = lds_addr(&sK[0][0]), sV0 = lds_addr(&sV[0][0]);
+  auto issue_k = [&](int tile) {
     const int kt = tile * BN;
+    const auto rs = make_rsrc(kh + (size_t)kt * D, (uint32_t)(min(BN, a.Sk - kt) * D * 2));
+    const uint32_t dst = sK0 + (tile & 1) * (TILE * 2);
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int e = tid + i * kThreads;
-      const int row = e / KCH, ch = e % KCH;
-      const int key = kt + row;
-      kr[i] = (key < a.Sk) ? *(const u32x4*)(a.k + (kv_base + key) * D + ch * 8) : u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < BPW; ++i) dma16(rs, koff[i], dst + (i * (kThreads / 64) + wave) * 1024);
+  };
+  auto issue_v = [&](int tile) {
+    const int kt = tile * BN;
+    const auto rs = make_rsrc(vh + (size_t)kt * D, (uint32_t)(min(BN, a.Sk - kt) * D * 2));
+    const uint32_t dst = sV0 + (tile & 1) * (TILE * 2);
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-      const int key = kt + vkg * KPT + e;
-      vr[e] = (key < a.Sk) ? *(const u32x4*)(a.v + (kv_base + key) * D + vch * 8) : u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < BPW; ++i) dma16(rs, voff[i], dst + (i * (kThreads / 64) + wave) * 1024);
   };
 
-  auto store = [&]() {
+  // does tile t hold any key visible to this wavefront's rows? all of them?
+  auto tile_any = [&](int tile) {
+    const int kt0 = tile * BN, kt1 = kt0 + BN - 1;
+    bool any = wave_live;
+    if (a.causal) any = any && (kt0 <= phi);
+    if (w >= 0) any = any && (kt1 >= plo - w) && (kt0 <= phi + w);
+    return any;
+  };
+  auto tile_full = [&](int tile) {
+    const int kt0 = tile * BN, kt1 = kt0 + BN - 1;
+    bool full = kt1 < a.Sk;
+    if (a.causal) full = full && (kt1 <= plo);
+    if (w >= 0) full = full && (kt0 >= phi - w) && (kt1 <= plo + w);
+    return full;
+  };
+
+  auto qk = [&](int tile, f32x16* st) {
+    const uint16_t* kb_base = &sK[tile & 1][0];
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int e = tid + i * kThreads;
-      const int row = e / KCH, ch = e % KCH;
-      const int lrow = key_slot(row);
-      const int pch = ch ^ (lrow & 7);
-      *(u32x4*)(sK + lrow * D + pch * 8) = kr[i];
-    }
-    // V^T: row d = 8*vch + i holds this thread's KPT keys at column vkg*KPT
-    const int kc = (vkg * KPT) / 8, kin = (vkg * KPT) % 8;
+    for (int kb = 0; kb < NKB; ++kb) {
+      st[kb] = f32x16{};
+      const int row = kb * 32 + l32;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int d = vch * 8 + i;
-      uint16_t* dst = sV + d * BN + ((kc ^ (d & 7)) * 8) + kin;
-      if constexpr (KPT == 4) {
-        u32x2 pr;
-        pr[0] = pick_pair(vr[0], vr[1], i);
-        pr[1] = pick_pair(vr[2], vr[3], i);
-        *(u32x2*)dst = pr;
-      } else {
-        *(uint32_t*)dst = pick_pair(vr[0], vr[1], i);
+      for (int t = 0; t < NQK; ++t) {
+        const bf16x8 kf = *(const bf16x8*)(kb_base + row * D + (((2 * t + hh) ^ swz_k<D>(row)) * 8));
+        st[kb] = mfma32(kf, qf[t], st[kb]);
       }
     }
   };
@@ -179,45 +210,34 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   f32x16 oacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
-  float m_run = kNegInf;  // running max of c2 * score (base-2 units)
+  float m_run = kNegInf;  // reference max of c2 * score (base-2 units)
   float l_run = 0.f;      // this lane's part of the running sum (its 16 keys per block)
   const float c2 = a.c2;
-  const int pos = qi + off;  // key position aligned with this lane's row
 
-  if (t_begin < t_end) fetch(t_begin);
-  for (int tile = t_begin; tile < t_end; ++tile) {
-    store();
+  f32x16 s_cur[NKB], s_nxt[NKB];
+  if (t_begin < t_end) {
+    issue_k(t_begin);
+    issue_v(t_begin);
+    if (t_begin + 1 < t_end) issue_k(t_begin + 1);
+    wait_vmcnt<0>();
     __syncthreads();
-    if (tile + 1 < t_end) fetch(tile + 1);
+    if (tile_any(t_begin)) qk(t_begin, s_cur);
+  }
+  for (int tile = t_begin; tile < t_end; ++tile) {
+    // K(tile+1) and V(tile) were issued one iteration ago; every wavefront
+    // has finished with K(tile) and V(tile-1), whose slots are refilled now.
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (tile + 2 < t_end) issue_k(tile + 2);
+    if (tile + 1 < t_end) issue_v(tile + 1);
 
-    const int kt0 = tile * BN, kt1 = kt0 + BN - 1;
-    const int plo = qw0 + off, phi = qw1 + off;
-    bool any = wave_live, full = kt1 < a.Sk;
-    if (a.causal) {
-      any = any && (kt0 <= phi);
-      full = full && (kt1 <= plo);
-    }
-    if (w >= 0) {
-      any = any && (kt1 >= plo - w) && (kt0 <= phi + w);
-      full = full && (kt0 >= phi - w) && (kt1 <= plo + w);
-    }
+    const bool nxt = (tile + 1 < t_end) && tile_any(tile + 1);
+    if (nxt) qk(tile + 1, s_nxt);
 
-    if (any) {
-      // S^T = K Q^T
-      f32x16 st[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        st[kb] = f32x16{};
-        const int lrow = kb * 32 + l32;
-#pragma unroll
-        for (int t = 0; t < NQK; ++t) {
-          const int pch = (2 * t + hh) ^ (lrow & 7);
-          const bf16x8 kf = *(const bf16x8*)(sK + lrow * D + pch * 8);
-          st[kb] = mfma32(kf, qf[t], st[kb]);
-        }
-      }
-      // key of accumulator r in block kb: kt0 + 32kb + 16(r/8) + 8hh + r%8
-      if (!full) {
+    if (tile_any(tile)) {
+      const int kt0 = tile * BN;
+      if (!tile_full(tile)) {
+        // key of accumulator r in block kb: kt0 + 32kb + 16(r/8) + 8hh + r%8
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -226,53 +246,63 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
             bool vis = key < a.Sk;
             if (a.causal) vis = vis && key <= pos;
             if (w >= 0) vis = vis && key >= pos - w && key <= pos + w;
-            st[kb][r] = vis ? st[kb][r] : kNegInf;
+            s_cur[kb][r] = vis ? s_cur[kb][r] : kNegInf;
           }
         }
       }
-      // online softmax (base 2)
       float mx = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
-      mx = fmaxf(mx, xor_shfl(mx, 32));
-      const float m_new = fmaxf(m_run, mx * c2);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kb][r]);
+      mx = fmaxf(mx, xor_shfl(mx, 32)) * c2;
+      if (__any(mx > m_run + kSlack)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == kNegInf) ? 0.f : m_run;
       float rs = 0.f;
+      bf16x8 pf[NKB][2];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(st[kb][r], c2, -m_use));
-          st[kb][r] = p;
+          const float p = fast_exp2(__builtin_fmaf(s_cur[kb][r], c2, -m_use));
           rs += p;
+          pf[kb][r >> 3][r & 7] = (__bf16)p;
         }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      l_run += rs;
 
-      // O^T += V^T P^T
+      // O^T += V^T P^T; the V^T operand for (db, kb, s) is two transposing
+      // reads of keys 32kb + 16s + 8hh + [0..3] and [4..7], dims 32db + l32.
+      const uint16_t* vb = &sV[tile & 1][0];
+      const int vr0 = 8 * hh + ((lane & 15) >> 2);
+      const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          bf16x8 pf;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) pf[j] = (__bf16)st[kb][8 * s + j];
-          const int ch = 4 * kb + 2 * s + hh;
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const int d = db * 32 + l32;
-            const bf16x8 vf = *(const bf16x8*)(sV + d * BN + ((ch ^ (d & 7)) * 8));
-            oacc[db] = mfma32(vf, pf, oacc[db]);
+            const int col = 32 * db + vcol;
+            const int ra = kb * 32 + 16 * s + vr0, rb = ra + 4;
+            const s16x4 lo = lds_read_tr16(vb + ra * D + ((col >> 3) ^ swz_v<D>(ra)) * 8 + (col & 7));
+            const s16x4 hi = lds_read_tr16(vb + rb * D + ((col >> 3) ^ swz_v<D>(rb)) * 8 + (col & 7));
+            const bf16x8 vf = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            oacc[db] = mfma32(vf, pf[kb][s], oacc[db]);
           }
         }
       }
     }
-    __syncthreads();
+    if (nxt) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s_cur[kb] = s_nxt[kb];
+    }
   }
 
   // ---- epilogue: normalise, round once to bf16, write o and lse ----------
@@ -321,7 +351,7 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
   if (s.D == 128)
     hipLaunchKernelGGL((fwd_bf16_kernel<128, 64>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<64, 128>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<64, 64>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
