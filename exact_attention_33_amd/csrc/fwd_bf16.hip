@@ -13,9 +13,8 @@
 //     each wavefront owns 32 rows.  Two workgroups share a CU.
 //   * K and V tiles of BN keys stream HBM -> LDS by buffer loads that write
 //     LDS directly (no register staging); out-of-range keys read as zero.
-//     K runs one tile ahead of V in two 2-slot rings, so while tile t is in
-//     its softmax, K(t+1) is already resident and K(t+2), V(t+1) are in
-//     flight.  One barrier per tile.
+//     Two slots each: tile t+1 is in flight while tile t is multiplied.
+//     One barrier per tile.
 //   * scores are computed transposed, S^T = K Q^T, on
 //     v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims from LDS, B = the Q
 //     fragment held in registers).  A lane then holds ONE query and 16 of a
@@ -27,8 +26,9 @@
 //     [key][dim] tile.  P lines up with V because K rows sit in LDS with bits
 //     2 and 3 of the key index swapped inside each 32-key block, which makes
 //     the 8 keys a lane holds for each 16-key step consecutive.
-//   * each wavefront issues the q k^T products of tile t+1 before the softmax
-//     of tile t, so the exponentials overlap matrix-core work.
+//   * two workgroups share each CU (one wavefront of each per SIMD) and are
+//     not coupled by barriers, so one wavefront's softmax overlaps the other's
+//     matrix-core work.
 //   * the running max is only raised when a row's new maximum exceeds it by
 //     more than kSlack (base-2 units); otherwise probabilities are taken
 //     against the old reference (bounded by 2^kSlack), which skips most
@@ -195,11 +195,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   auto qk = [&](int tile, f32x16* st) {
     const uint16_t* kb_base = &sK[tile & 1][0];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      st[kb] = f32x16{};
-      const int row = kb * 32 + l32;
+    for (int kb = 0; kb < NKB; ++kb) st[kb] = f32x16{};
 #pragma unroll
-      for (int t = 0; t < NQK; ++t) {
+    for (int t = 0; t < NQK; ++t) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int row = kb * 32 + l32;
         const bf16x8 kf = *(const bf16x8*)(kb_base + row * D + (((2 * t + hh) ^ swz_k<D>(row)) * 8));
         st[kb] = mfma32(kf, qf[t], st[kb]);
       }
@@ -213,95 +214,96 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   float m_run = kNegInf;  // reference max of c2 * score (base-2 units)
   float l_run = 0.f;      // this lane's part of the running sum (its 16 keys per block)
   const float c2 = a.c2;
-
-  f32x16 s_cur[NKB], s_nxt[NKB];
-  if (t_begin < t_end) {
-    issue_k(t_begin);
-    issue_v(t_begin);
-    if (t_begin + 1 < t_end) issue_k(t_begin + 1);
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (tile_any(t_begin)) qk(t_begin, s_cur);
+  // keys visible to this lane's row form [key_lo, key_hi] (empty if hi < lo)
+  int key_lo = 0, key_hi = a.Sk - 1;
+  if (a.causal) key_hi = min(key_hi, pos);
+  if (w >= 0) {
+    key_lo = max(key_lo, pos - w);
+    key_hi = min(key_hi, pos + w);
   }
-  for (int tile = t_begin; tile < t_end; ++tile) {
-    // K(tile+1) and V(tile) were issued one iteration ago; every wavefront
-    // has finished with K(tile) and V(tile-1), whose slots are refilled now.
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (tile + 2 < t_end) issue_k(tile + 2);
-    if (tile + 1 < t_end) issue_v(tile + 1);
 
-    const bool nxt = (tile + 1 < t_end) && tile_any(tile + 1);
-    if (nxt) qk(tile + 1, s_nxt);
-
-    if (tile_any(tile)) {
-      const int kt0 = tile * BN;
-      if (!tile_full(tile)) {
-        // key of accumulator r in block kb: kt0 + 32kb + 16(r/8) + 8hh + r%8
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kt0 + kb * 32 + 16 * (r >> 3) + 8 * hh + (r & 7);
-            bool vis = key < a.Sk;
-            if (a.causal) vis = vis && key <= pos;
-            if (w >= 0) vis = vis && key >= pos - w && key <= pos + w;
-            s_cur[kb][r] = vis ? s_cur[kb][r] : kNegInf;
-          }
-        }
-      }
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kb][r]);
-      mx = fmaxf(mx, xor_shfl(mx, 32)) * c2;
-      if (__any(mx > m_run + kSlack)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-      float rs = 0.f;
-      bf16x8 pf[NKB][2];
+  // softmax of one tile's scores (in place -> probabilities) and O += V^T P^T
+  auto softmax_pv = [&](int tile, f32x16* st) {
+    const int kt0 = tile * BN;
+    if (!tile_full(tile)) {
+      // accumulator r of block kb holds key kt0 + 8hh + c with c = 32kb + 16(r/8) + r%8
+      const int lo = key_lo - kt0 - 8 * hh, hi = key_hi - kt0 - 8 * hh;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(s_cur[kb][r], c2, -m_use));
-          rs += p;
-          pf[kb][r >> 3][r & 7] = (__bf16)p;
+          const int c = kb * 32 + 16 * (r >> 3) + (r & 7);
+          st[kb][r] = ((c >= lo) & (c <= hi)) ? st[kb][r] : kNegInf;
         }
-      l_run += rs;
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
+    mx = fmaxf(mx, xor_shfl(mx, 32)) * c2;
+    if (__any(mx > m_run + kSlack)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+    float rs = 0.f;
+    bf16x8 pf[NKB][2];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(__builtin_fmaf(st[kb][r], c2, -m_use));
+        rs += p;
+        pf[kb][r >> 3][r & 7] = (__bf16)p;
+      }
+    l_run += rs;
 
-      // O^T += V^T P^T; the V^T operand for (db, kb, s) is two transposing
-      // reads of keys 32kb + 16s + 8hh + [0..3] and [4..7], dims 32db + l32.
-      const uint16_t* vb = &sV[tile & 1][0];
-      const int vr0 = 8 * hh + ((lane & 15) >> 2);
-      const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // O^T += V^T P^T; the V^T operand for (db, kb, s) is two transposing
+    // reads of keys 32kb + 16s + 8hh + [0..3] and [4..7], dims 32db + l32.
+    const uint16_t* vb = &sV[tile & 1][0];
+    const int vr0 = 8 * hh + ((lane & 15) >> 2);
+    const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+      for (int s = 0; s < 2; ++s) {
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const int col = 32 * db + vcol;
-            const int ra = kb * 32 + 16 * s + vr0, rb = ra + 4;
-            const s16x4 lo = lds_read_tr16(vb + ra * D + ((col >> 3) ^ swz_v<D>(ra)) * 8 + (col & 7));
-            const s16x4 hi = lds_read_tr16(vb + rb * D + ((col >> 3) ^ swz_v<D>(rb)) * 8 + (col & 7));
-            const bf16x8 vf = __builtin_bit_cast(
-                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            oacc[db] = mfma32(vf, pf[kb][s], oacc[db]);
-          }
+        for (int db = 0; db < NDB; ++db) {
+          const int col = 32 * db + vcol;
+          const int ra = kb * 32 + 16 * s + vr0, rb = ra + 4;
+          const s16x4 lo4 = lds_read_tr16(vb + ra * D + ((col >> 3) ^ swz_v<D>(ra)) * 8 + (col & 7));
+          const s16x4 hi4 = lds_read_tr16(vb + rb * D + ((col >> 3) ^ swz_v<D>(rb)) * 8 + (col & 7));
+          const bf16x8 vf = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[db] = mfma32(vf, pf[kb][s], oacc[db]);
         }
       }
     }
-    if (nxt) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s_cur[kb] = s_nxt[kb];
+  };
+
+  // K(t) and V(t) land in slot t&1; the loads of tile t+1 are issued as soon
+  // as every wavefront is done with tile t-1 (the barrier), so they fly while
+  // tile t is multiplied.
+  if (t_begin < t_end) {
+    issue_k(t_begin);
+    issue_v(t_begin);
+  }
+  for (int tile = t_begin; tile < t_end; ++tile) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (tile + 1 < t_end) {
+      issue_k(tile + 1);
+      issue_v(tile + 1);
+    }
+    if (tile_any(tile)) {
+      f32x16 st[NKB];
+      qk(tile, st);
+      softmax_pv(tile, st);
     }
   }
 
