@@ -8,6 +8,7 @@ namespace ea {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -47,6 +48,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // bytes land at LDS byte address lds_base + 16*i (lds_base wave-uniform).
 // Issued from asm so the compiler does not guard later LDS reads with a
 // blanket vmcnt(0); completion is awaited explicitly (vmcnt) by the caller.
+// The block sets M0 itself right before the load; the compiler treats M0 as
+// reserved and ignores the clobber, and no compiler-generated code in these
+// kernels reads M0 (checked in the emitted ISA), so nothing depends on its
+// value across blocks.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(lds_base), "v"(voff), "s"(rs) : "memory", "m0");

@@ -28,7 +28,10 @@
 //     the 8 keys a lane holds for each 16-key step consecutive.
 //   * two workgroups share each CU (one wavefront of each per SIMD) and are
 //     not coupled by barriers, so one wavefront's softmax overlaps the other's
-//     matrix-core work.
+//     matrix-core work.  The tile loop body is branch-free apart from the
+//     rare wave-uniform rescale (a tile no row of the wavefront can see is
+//     simply masked to zero weight), which keeps the accumulators in place:
+//     no register copies at control-flow joins.
 //   * the running max is only raised when a row's new maximum exceeds it by
 //     more than kSlack (base-2 units); otherwise probabilities are taken
 //     against the old reference (bounded by 2^kSlack), which skips most
@@ -136,7 +139,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int qw1 = min(qw0 + 31, a.Sq - 1);      // last valid row
   const int qi = qw0 + l32;                     // this lane's row
   const bool q_ok = qi < a.Sq;
-  const bool wave_live = qw0 < a.Sq;
   const int pos = qi + off;                     // key position aligned with the row
   const int plo = qw0 + off, phi = qw1 + off;
 
@@ -176,14 +178,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     for (int i = 0; i < BPW; ++i) dma16(rs, voff[i], dst + (i * (kThreads / 64) + wave) * 1024);
   };
 
-  // does tile t hold any key visible to this wavefront's rows? all of them?
-  auto tile_any = [&](int tile) {
-    const int kt0 = tile * BN, kt1 = kt0 + BN - 1;
-    bool any = wave_live;
-    if (a.causal) any = any && (kt0 <= phi);
-    if (w >= 0) any = any && (kt1 >= plo - w) && (kt0 <= phi + w);
-    return any;
-  };
+  // does every row of this wavefront see every key of tile t?
   auto tile_full = [&](int tile) {
     const int kt0 = tile * BN, kt1 = kt0 + BN - 1;
     bool full = kt1 < a.Sk;
@@ -192,16 +187,35 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     return full;
   };
 
-  auto qk = [&](int tile, f32x16* st) {
-    const uint16_t* kb_base = &sK[tile & 1][0];
+  // Lane-constant byte offsets of the MFMA operand reads inside one LDS slot.
+  // The swizzles only depend on row bits that do not change between 32-key
+  // blocks, so block / step offsets become immediates of the ds_read.
+  uint32_t ka[NQK];
+#pragma unroll
+  for (int t = 0; t < NQK; ++t)
+    ka[t] = (uint32_t)(l32 * D * 2 + (((2 * t + hh) ^ swz_k<D>(l32)) * 16));
+  const int vr0 = 8 * hh + ((lane & 15) >> 2);
+  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  uint32_t va[2][2][NDB];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int row = 16 * s2 + vr0 + 4 * r2, col = 32 * db + vcol;
+        va[s2][r2][db] = (uint32_t)(row * D * 2 + (((col >> 3) ^ swz_v<D>(row)) * 16) + (col & 7) * 2);
+      }
+
+  auto qk = [&](int slot, f32x16* st) {
+    const char* kb_base = (const char*)&sK[0][0] + slot * (TILE * 2);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) st[kb] = f32x16{};
 #pragma unroll
     for (int t = 0; t < NQK; ++t) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const int row = kb * 32 + l32;
-        const bf16x8 kf = *(const bf16x8*)(kb_base + row * D + (((2 * t + hh) ^ swz_k<D>(row)) * 8));
+        const bf16x8 kf = *(const bf16x8*)(kb_base + ka[t] + kb * 32 * D * 2);
         st[kb] = mfma32(kf, qf[t], st[kb]);
       }
     }
@@ -223,7 +237,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   }
 
   // softmax of one tile's scores (in place -> probabilities) and O += V^T P^T
-  auto softmax_pv = [&](int tile, f32x16* st) {
+  auto softmax_pv = [&](int slot, int tile, f32x16* st) {
     const int kt0 = tile * BN;
     if (!tile_full(tile)) {
       // accumulator r of block kb holds key kt0 + 8hh + c with c = 32kb + 16(r/8) + r%8
@@ -265,22 +279,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 
     // O^T += V^T P^T; the V^T operand for (db, kb, s) is two transposing
     // reads of keys 32kb + 16s + 8hh + [0..3] and [4..7], dims 32db + l32.
-    const uint16_t* vb = &sV[tile & 1][0];
-    const int vr0 = 8 * hh + ((lane & 15) >> 2);
-    const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const char* vb = (const char*)&sV[0][0] + slot * (TILE * 2);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int col = 32 * db + vcol;
-          const int ra = kb * 32 + 16 * s + vr0, rb = ra + 4;
-          const s16x4 lo4 = lds_read_tr16(vb + ra * D + ((col >> 3) ^ swz_v<D>(ra)) * 8 + (col & 7));
-          const s16x4 hi4 = lds_read_tr16(vb + rb * D + ((col >> 3) ^ swz_v<D>(rb)) * 8 + (col & 7));
+          const char* p0 = vb + kb * 32 * D * 2;
+          const s16x4 lo4 = lds_read_tr16((const uint16_t*)(p0 + va[s2][0][db]));
+          const s16x4 hi4 = lds_read_tr16((const uint16_t*)(p0 + va[s2][1][db]));
           const bf16x8 vf = __builtin_bit_cast(
               bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[db] = mfma32(vf, pf[kb][s], oacc[db]);
+          oacc[db] = mfma32(vf, pf[kb][s2], oacc[db]);
         }
       }
     }
@@ -300,10 +311,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
       issue_k(tile + 1);
       issue_v(tile + 1);
     }
-    if (tile_any(tile)) {
+    {
+      // a tile no row of this wavefront can see is masked to zero weight
       f32x16 st[NKB];
-      qk(tile, st);
-      softmax_pv(tile, st);
+      qk(tile & 1, st);
+      softmax_pv(tile & 1, tile, st);
     }
   }
 
