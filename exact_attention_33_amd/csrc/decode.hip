@@ -21,12 +21,13 @@
 // The 4 wavefront partials are merged in LDS ((w0+w1)+(w2+w3)) and one
 // partial per head is written: acc unnormalised, m in base-2 units.
 //
-// Combine kernel: one workgroup per (b, h, group of <= 256 partials, 64 dims).
-// Partials are loaded into LDS and merged level by level: at stride s the
-// partial at index i (i a multiple of 2s) absorbs index i+s; an index with
-// no partner passes up unchanged.  The root is normalised (o = acc / l,
-// lse = ln2 * (m + log2 l)) and written, or, above 256 partials, written as
-// one partial of the next tree level.
+// Combine kernel: one workgroup per (b, h, group of <= 256 partials).  The
+// partials are merged level by level: at stride s the partial at index i (i a
+// multiple of 2s) absorbs index i+s; an index with no partner passes up
+// unchanged.  Strides 1..32 run in registers within a wavefront (64 partials
+// each), strides 64 and 128 across the four wavefronts in LDS.  The root is
+// normalised (o = acc / l, lse = ln2 * (m + log2 l)) and written, or, above
+// 256 partials, written as one partial of the next tree level.
 #include "common.h"
 #include "kernels.h"
 
@@ -47,7 +48,7 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
   constexpr int NT = D / 32;  // k-steps of s^T = K q^T
   constexpr int VE = D / 16;  // dims of V per lane per key; also MFMAs per step of o^T
-  __shared__ float sO[4][16][D];
+  __shared__ float sO[4][16][D + 1];  // +1: the per-lane strided stores hit distinct banks
   __shared__ float sM[4][16];
   __shared__ float sL[4][16];
 
@@ -193,8 +194,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
   }
 }
 
-constexpr int kGroup = 256;  // partials merged by one combine workgroup
-constexpr int kDSlice = 64;  // dims per combine workgroup
+constexpr int kLeaves = 64;   // partials merged in registers by one wavefront
+constexpr int kGroup = 256;   // partials merged by one combine workgroup (4 wavefronts)
 
 struct CombineArgs {
   const float* in_o;   // [BH][n][D]
@@ -203,69 +204,103 @@ struct CombineArgs {
   float* out_ml;
   uint16_t* o;         // final: bf16 [BH][D]
   float* lse;          // final: fp32 [BH] or null
-  int n, ngroups, D, final_pass;
+  int n, ngroups, final_pass;
 };
 
+__device__ __forceinline__ float lane_value(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
+// One workgroup per (b*h, group of <= 256 partials).  Wavefront w owns leaves
+// 64w .. 64w+63 of the group: lane i holds (m, l) of leaf i and, for every
+// leaf, this lane's D/64 dims of the accumulator.  The leaves are merged in
+// registers level by level (stride 1, 2, ..., 32: leaf i absorbs leaf i+s
+// when i is a multiple of 2s); leaves past the end are the merge identity, so
+// an unpaired partial passes up unchanged.  The four wavefront roots are then
+// merged in LDS at strides 64 and 128, which completes the balanced binary
+// tree over the group's partials.
+template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  __shared__ float sO[kGroup][kDSlice];
-  __shared__ float sM[kGroup], sL[kGroup];
-  __shared__ float sFa[kGroup / 2], sFb[kGroup / 2];
+  constexpr int DPL = D / 64;  // dims per lane
+  __shared__ float sO[4][D];
+  __shared__ float sM[4], sL[4];
 
-  const int nds = a.D / kDSlice;
-  int bid = blockIdx.x;
-  const int ds = bid % nds;
-  bid /= nds;
-  const int grp = bid % a.ngroups;
-  const int bh = bid / a.ngroups;
-  const int tid = threadIdx.x;
-  const int i0 = grp * kGroup;
-  const int ng = min(kGroup, a.n - i0);
-  const size_t base = (size_t)bh * a.n + i0;
+  const int grp = blockIdx.x % a.ngroups;
+  const int bh = blockIdx.x / a.ngroups;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int base = grp * kGroup + wave * kLeaves;
+  const int nl = max(0, min(kLeaves, a.n - base));
+  const size_t row0 = (size_t)bh * a.n + base;
 
-  for (int it = tid; it < ng * kDSlice; it += 256) {
-    const int i = it / kDSlice, d = it % kDSlice;
-    sO[i][d] = a.in_o[(base + i) * a.D + ds * kDSlice + d];
+  float m = kNegInf, l = 0.f;
+  float o[kLeaves][DPL];
+#pragma unroll
+  for (int i = 0; i < kLeaves; ++i)
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) o[i][j] = 0.f;
+  if (nl > 0) {
+    if (lane < nl) {
+      m = a.in_ml[(row0 + lane) * 2];
+      l = a.in_ml[(row0 + lane) * 2 + 1];
+    }
+#pragma unroll
+    for (int i = 0; i < kLeaves; ++i) {
+      const float* src = a.in_o + (row0 + min(i, nl - 1)) * D + lane * DPL;
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) o[i][j] = (i < nl) ? src[j] : 0.f;
+    }
   }
-  for (int i = tid; i < ng; i += 256) {
-    sM[i] = a.in_ml[(base + i) * 2];
-    sL[i] = a.in_ml[(base + i) * 2 + 1];
+
+#pragma unroll
+  for (int s = 1; s < kLeaves; s *= 2) {
+    const float mj = __shfl_down(m, s, 64);
+    const float lj = __shfl_down(l, s, 64);
+    const MergeFactors f = merge_factors(m, mj);
+    const bool leader = (lane & (2 * s - 1)) == 0;
+#pragma unroll
+    for (int i = 0; i < kLeaves; i += 2 * s) {
+      const float fa = lane_value(f.fa, i), fb = lane_value(f.fb, i);
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) o[i][j] = o[i][j] * fa + o[i + s][j] * fb;
+    }
+    l = leader ? l * f.fa + lj * f.fb : l;
+    m = leader ? f.m : m;
   }
+
+  if (lane == 0) {
+    sM[wave] = m;
+    sL[wave] = l;
+  }
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) sO[wave][lane * DPL + j] = o[0][j];
   __syncthreads();
+  if (wave != 0) return;
 
-  for (int s = 1; s < ng; s *= 2) {
-    const int npairs = (ng - s + 2 * s - 1) / (2 * s);
-    for (int p = tid; p < npairs; p += 256) {
-      const int i = 2 * s * p, j = i + s;
-      const MergeFactors f = merge_factors(sM[i], sM[j]);
-      sFa[p] = f.fa;
-      sFb[p] = f.fb;
-      sL[i] = sL[i] * f.fa + sL[j] * f.fb;
-      sM[i] = f.m;
-    }
-    __syncthreads();
-    for (int it = tid; it < npairs * kDSlice; it += 256) {
-      const int p = it / kDSlice, d = it % kDSlice;
-      const int i = 2 * s * p, j = i + s;
-      sO[i][d] = sO[i][d] * sFa[p] + sO[j][d] * sFb[p];
-    }
-    __syncthreads();
-  }
-
-  if (tid < kDSlice) {
-    const float M = sM[0], L = sL[0], acc = sO[0][tid];
+  const MergeFactors f01 = merge_factors(sM[0], sM[1]);
+  const MergeFactors f23 = merge_factors(sM[2], sM[3]);
+  const MergeFactors fr = merge_factors(f01.m, f23.m);
+  const float M = fr.m;
+  const float L = (sL[0] * f01.fa + sL[1] * f01.fb) * fr.fa + (sL[2] * f23.fa + sL[3] * f23.fb) * fr.fb;
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) {
+    const int d = lane * DPL + j;
+    const float acc = (sO[0][d] * f01.fa + sO[1][d] * f01.fb) * fr.fa +
+                      (sO[2][d] * f23.fa + sO[3][d] * f23.fb) * fr.fb;
     if (a.final_pass) {
-      const float ov = (L > 0.f) ? acc / L : 0.f;
-      const __bf16 ob = (__bf16)ov;
-      a.o[(size_t)bh * a.D + ds * kDSlice + tid] = __builtin_bit_cast(uint16_t, ob);
-      if (a.lse != nullptr && ds == 0 && tid == 0)
-        a.lse[bh] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
+      const __bf16 ob = (__bf16)((L > 0.f) ? acc / L : 0.f);
+      a.o[(size_t)bh * D + d] = __builtin_bit_cast(uint16_t, ob);
+    } else {
+      a.out_o[((size_t)bh * a.ngroups + grp) * D + d] = acc;
+    }
+  }
+  if (lane == 0) {
+    if (a.final_pass) {
+      if (a.lse != nullptr) a.lse[bh] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
     } else {
       const size_t slot = (size_t)bh * a.ngroups + grp;
-      a.out_o[slot * a.D + ds * kDSlice + tid] = acc;
-      if (ds == 0 && tid == 0) {
-        a.out_ml[slot * 2] = M;
-        a.out_ml[slot * 2 + 1] = L;
-      }
+      a.out_ml[slot * 2] = M;
+      a.out_ml[slot * 2 + 1] = L;
     }
   }
 }
@@ -318,14 +353,16 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v
     c.in_ml = in_ml;
     c.n = n;
     c.ngroups = (n + kGroup - 1) / kGroup;
-    c.D = s.D;
     c.final_pass = c.ngroups == 1;
     c.out_o = next;
     c.out_ml = next + (size_t)BH * c.ngroups * s.D;
     c.o = o;
     c.lse = lse;
-    dim3 cgrid((unsigned)((int64_t)BH * c.ngroups * (s.D / kDSlice)));
-    hipLaunchKernelGGL(combine_kernel, cgrid, dim3(256), 0, stream, c);
+    dim3 cgrid((unsigned)((int64_t)BH * c.ngroups));
+    if (s.D == 128)
+      hipLaunchKernelGGL((combine_kernel<128>), cgrid, dim3(256), 0, stream, c);
+    else
+      hipLaunchKernelGGL((combine_kernel<64>), cgrid, dim3(256), 0, stream, c);
     err = hipGetLastError();
     if (err != hipSuccess || c.final_pass) return err;
     in_o = c.out_o;
