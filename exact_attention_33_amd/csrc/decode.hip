@@ -9,6 +9,9 @@
 // every query head that shares the kv head (GQA), which keeps the kernel at
 // one read of the cache -- the quantity that bounds decode.  Each of the 4
 // wavefronts takes every 4th 32-key step of the chunk:
+//   * K and V are read with buffer loads over exactly the step's keys inside
+//     the chunk: keys past the chunk end read as zero with no branch, and the
+//     per-lane offsets are immediates of the load instructions;
 //   * s^T = K q^T on v_mfma_f32_16x16x32_bf16, K loaded straight from HBM
 //     into the A-operand layout (16 keys x 32 dims, 16 bytes per lane), the
 //     query heads as the 16 columns of B (unused columns are zero);
@@ -89,33 +92,42 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
   // A-operand row i of key block a2 reads key 8*(i/4) + 4*a2 + i%4 of the step,
   // so lane group q4 ends up holding keys 8*q4 .. 8*q4+7 of the step.
   const int krow = 8 * (hc >> 2) + (hc & 3);
+  // per-lane byte offsets inside one 32-key step; the rest are immediates
+  const uint32_t koff = (uint32_t)((krow * D + 8 * q4) * 2);
+  const uint32_t voff = (uint32_t)((8 * q4 * D + VE * hc) * 2);
 
-  for (int kw = c0 + 32 * wave; kw < c1; kw += 128) {
-    u32x4 kf[2][NT];
+  // One 32-key step's K and V for this lane.  The buffer covers only the
+  // keys of the step that lie inside the chunk, so keys past the chunk end
+  // (or a step entirely past it) read as zero without a branch.
+  struct StepRegs {
+    u32x4 k[2][NT];
+    uint32_t v[8][VE / 2];
+  };
+  auto load_step = [&](StepRegs& r, int kw) {
+    const int nk = max(0, min(32, c1 - kw));
+    const auto rk = make_rsrc(a.k + (kvb + (size_t)min(kw, c1)) * D, (uint32_t)(nk * D * 2));
+    const auto rv = make_rsrc(a.v + (kvb + (size_t)min(kw, c1)) * D, (uint32_t)(nk * D * 2));
 #pragma unroll
-    for (int a2 = 0; a2 < 2; ++a2) {
-      const int key = kw + krow + 4 * a2;
+    for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
       for (int t = 0; t < NT; ++t)
-        kf[a2][t] = (key < c1) ? *(const u32x4*)(a.k + (kvb + key) * D + 32 * t + 8 * q4)
-                               : u32x4{0, 0, 0, 0};
-    }
-    uint32_t vf[8][VE / 2];
+        r.k[a2][t] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + (4 * a2 * D + 32 * t) * 2, 0, 0);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int key = kw + 8 * q4 + e;
-      const uint16_t* src = a.v + (kvb + key) * D + VE * hc;
       if constexpr (VE == 8) {
-        u32x4 x = (key < c1) ? *(const u32x4*)src : u32x4{0, 0, 0, 0};
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + e * D * 2, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vf[e][i] = x[i];
+        for (int i = 0; i < 4; ++i) r.v[e][i] = x[i];
       } else {
-        u32x2 x = (key < c1) ? *(const u32x2*)src : u32x2{0, 0};
+        const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rv, voff + e * D * 2, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) vf[e][i] = x[i];
+        for (int i = 0; i < 2; ++i) r.v[e][i] = x[i];
       }
     }
+  };
 
+  // scores, online softmax and o^T += V^T p^T for one step (keys >= c1 masked)
+  auto compute_step = [&](const StepRegs& r, int kw) {
     // s^T: lane holds head hc and keys kw + 8*q4 + 4*a2 + r
     f32x4 st[2];
 #pragma unroll
@@ -123,16 +135,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
       st[a2] = f32x4{};
 #pragma unroll
       for (int t = 0; t < NT; ++t)
-        st[a2] = mfma16(__builtin_bit_cast(bf16x8, kf[a2][t]), qf[t], st[a2]);
+        st[a2] = mfma16(__builtin_bit_cast(bf16x8, r.k[a2][t]), qf[t], st[a2]);
     }
     float mx = kNegInf;
 #pragma unroll
     for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kw + 8 * q4 + 4 * a2 + r;
-        st[a2][r] = (key < c1) ? st[a2][r] : kNegInf;
-        mx = fmaxf(mx, st[a2][r]);
+      for (int i = 0; i < 4; ++i) {
+        const int key = kw + 8 * q4 + 4 * a2 + i;
+        st[a2][i] = (key < c1) ? st[a2][i] : kNegInf;
+        mx = fmaxf(mx, st[a2][i]);
       }
     mx = fmaxf(mx, xor_shfl(mx, 16));
     mx = fmaxf(mx, xor_shfl(mx, 32));
@@ -144,10 +156,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
 #pragma unroll
     for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(__builtin_fmaf(st[a2][r], c2, -m_use));
+      for (int i = 0; i < 4; ++i) {
+        const float p = fast_exp2(__builtin_fmaf(st[a2][i], c2, -m_use));
         rs += p;
-        pf[4 * a2 + r] = (__bf16)p;
+        pf[4 * a2 + i] = (__bf16)p;
       }
     l_run = l_run * alpha + rs;
     m_run = m_new;
@@ -157,10 +169,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
       u32x4 t;
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2)
-        t[e2] = (j & 1) ? pack_hi(vf[2 * e2][j >> 1], vf[2 * e2 + 1][j >> 1])
-                        : pack_lo(vf[2 * e2][j >> 1], vf[2 * e2 + 1][j >> 1]);
+        t[e2] = (j & 1) ? pack_hi(r.v[2 * e2][j >> 1], r.v[2 * e2 + 1][j >> 1])
+                        : pack_lo(r.v[2 * e2][j >> 1], r.v[2 * e2 + 1][j >> 1]);
       oacc[j] = mfma16(__builtin_bit_cast(bf16x8, t), pf, oacc[j] * alpha);
     }
+  };
+
+  for (int kw = c0 + 32 * wave; kw < c1; kw += 128) {
+    StepRegs r;
+    load_step(r, kw);
+    compute_step(r, kw);
   }
 
   // lane (hc, q4) holds dims VE*(4*q4 + r) + j of head hc; l summed over q4
