@@ -40,8 +40,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // Buffer resource over [base, base + bytes): loads past the end return 0.
+// Callers pass wave-uniform values; readfirstlane makes that explicit so the
+// descriptor always lives in scalar registers.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* pu = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(pu, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           0x00020000);
 }
 
 // One 16-byte-per-lane load from a buffer straight into LDS: lane i's 16
@@ -54,7 +61,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // value across blocks.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds_base), "v"(voff), "s"(rs) : "memory", "m0");
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(rs) : "memory", "m0");
 }
 
 // Wait until at most N vector-memory loads of this wave are outstanding.

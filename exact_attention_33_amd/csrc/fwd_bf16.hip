@@ -219,6 +219,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
         st[kb] = mfma32(kf, qf[t], st[kb]);
       }
     }
+    // issue order: NQK reads, then read/MFMA pairs, then the remaining MFMAs,
+    // so every MFMA's operand was requested NQK reads earlier
+    __builtin_amdgcn_sched_group_barrier(0x100, NQK, 0);
+#pragma unroll
+    for (int i = 0; i < NQK * NKB - NQK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NQK, 0);
   };
 
   // ---- main loop ----------------------------------------------------------
