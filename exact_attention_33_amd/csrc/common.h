@@ -80,6 +80,16 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
 // Value of lane (lane ^ mask) within the wavefront.
 __device__ __forceinline__ float xor_shfl(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
+// max / sum of x over lanes l and l^32 (v_permlane32_swap, no LDS traffic)
+__device__ __forceinline__ float max_swap32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_swap32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Two bf16 (low halves / high halves of two packed words) into one word:
 // result.lo = x.half, result.hi = y.half.
 __device__ __forceinline__ uint32_t pack_lo(uint32_t x, uint32_t y) {

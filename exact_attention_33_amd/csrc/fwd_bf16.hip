@@ -36,9 +36,13 @@
 //     more than kSlack (base-2 units); otherwise probabilities are taken
 //     against the old reference (bounded by 2^kSlack), which skips most
 //     rescales of the accumulator.  The result is the same exact quantity.
-//   * LDS tiles are XOR-swizzled on 16-byte chunks (the buffer loads fetch
-//     the permuted source chunk per lane) so the MFMA operand reads are free
-//     of bank conflicts.
+//   * LDS layout (D = 128): rows are padded (K: 272 bytes, V: 320 bytes) so
+//     the MFMA operand reads are free of bank conflicts and every read
+//     address is one lane base plus an immediate offset.  D = 64 tiles are
+//     dense and XOR-swizzled on 16-byte chunks instead (the buffer loads
+//     fetch the permuted source chunk per lane).
+//   * the row max needs one exchange between lanes l and l^32
+//     (v_permlane32_swap); no LDS traffic.
 //   * all softmax arithmetic is base 2: scores are multiplied by
 //     scale*log2(e) inside one FMA, exponentials use v_exp_f32.
 #include "common.h"
@@ -84,16 +88,20 @@ __device__ __forceinline__ int swz_v(int row) {
 template <int D, int BN>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int KCH = D / 8;                      // 16-byte chunks per row
-  constexpr int TILE = BN * D;                    // bf16 per K or V tile
-  constexpr int NBLK = TILE * 2 / 1024;           // 1 KB load blocks per tile
-  constexpr int BPW = NBLK / (kThreads / 64);     // blocks per wavefront
   constexpr int NKB = BN / 32;                    // 32-key blocks per tile
   constexpr int NDB = D / 32;                     // 32-dim blocks of the output
   constexpr int NQK = D / 16;                     // k-steps of q k^T
-  static_assert(NBLK % 4 == 0, "tile must split into whole 1 KB blocks per wavefront");
 
-  __shared__ __attribute__((aligned(1024))) uint16_t sK[2][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV[2][TILE];
+  // padded rows (D = 128): operand addresses are a lane base plus immediates
+  constexpr bool PAD = (D == 128);
+  constexpr int KS = PAD ? D * 2 + 16 : D * 2;   // LDS row strides (bytes)
+  constexpr int VS = PAD ? D * 2 + 64 : D * 2;
+  constexpr int KSLOT = BN * KS, VSLOT = BN * VS;
+  constexpr int NB = (KSLOT + VSLOT) / 1024;     // 1 KB DMA blocks per (K, V) tile pair
+  constexpr int NBW = (NB + 3) / 4;              // per wavefront (at most)
+  static_assert(KSLOT % 1024 == 0 && VSLOT % 1024 == 0, "whole blocks");
+  __shared__ __attribute__((aligned(1024))) char sK[2 * KSLOT];
+  __shared__ __attribute__((aligned(1024))) char sV[2 * VSLOT];
 
   // ---- which (b, h, query tile) this workgroup computes -----------------
   const int BH = a.B * a.Hq;
@@ -154,28 +162,49 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   }
 
   // ---- tile loads: per-lane source offsets are the same for every tile ----
-  uint32_t koff[BPW], voff[BPW];
+  // block bb < KSLOT/1024 of a tile pair is a K block, the rest V blocks;
+  // wavefront w issues blocks w, w+4, ...
+  uint32_t doff[NBW], ddst[NBW];
+  bool disk[NBW];
 #pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    const int p = (i * (kThreads / 64) + wave) * 64 + lane;  // 16-byte slot in the tile
-    const int row = p / KCH, pch = p % KCH;
-    koff[i] = (uint32_t)((key_slot(row) * D + (pch ^ swz_k<D>(row)) * 8) * 2);
-    voff[i] = (uint32_t)((row * D + (pch ^ swz_v<D>(row)) * 8) * 2);
+  for (int i = 0; i < NBW; ++i) {
+    const int bb = i * 4 + wave;
+    disk[i] = bb < KSLOT / 1024;
+    if (disk[i]) {
+      const int p = bb * 64 + lane;
+      if constexpr (PAD) {
+        const int row = p / (KS / 16), u = p % (KS / 16);
+        doff[i] = (u < 16) ? (uint32_t)((key_slot(row) * D + u * 8) * 2) : 0x7ffffff0u;
+      } else {
+        const int row = p / KCH, pch = p % KCH;
+        doff[i] = (uint32_t)((key_slot(row) * D + (pch ^ swz_k<D>(row)) * 8) * 2);
+      }
+      ddst[i] = (uint32_t)(bb * 1024);
+    } else {
+      const int vb = bb - KSLOT / 1024;
+      const int p = vb * 64 + lane;
+      if constexpr (PAD) {
+        const int row = p / (VS / 16), u = p % (VS / 16);
+        doff[i] = (u < 16 && row < BN) ? (uint32_t)((row * D + u * 8) * 2) : 0x7ffffff0u;
+      } else {
+        const int row = p / KCH, pch = p % KCH;
+        doff[i] = (uint32_t)((row * D + (pch ^ swz_v<D>(row)) * 8) * 2);
+      }
+      ddst[i] = (uint32_t)(vb * 1024);
+    }
   }
-  const uint32_t sK0 = lds_addr(&sK[0][0]), sV0 = lds_addr(&sV[0][0]);
-  auto issue_k = [&](int tile) {
+  const int nbw = (NB - wave + 3) / 4;   // blocks this wavefront issues
+  const uint32_t sK0 = lds_addr(sK), sV0 = lds_addr(sV);
+  auto issue = [&](int tile) {
     const int kt = tile * BN;
-    const auto rs = make_rsrc(kh + (size_t)kt * D, (uint32_t)(min(BN, a.Sk - kt) * D * 2));
-    const uint32_t dst = sK0 + (tile & 1) * (TILE * 2);
+    const uint32_t bytes = (uint32_t)(min(BN, a.Sk - kt) * D * 2);
+    const auto rk = make_rsrc(kh + (size_t)kt * D, bytes);
+    const auto rv = make_rsrc(vh + (size_t)kt * D, bytes);
+    const uint32_t kdst = sK0 + (tile & 1) * KSLOT, vdst = sV0 + (tile & 1) * VSLOT;
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) dma16(rs, koff[i], dst + (i * (kThreads / 64) + wave) * 1024);
-  };
-  auto issue_v = [&](int tile) {
-    const int kt = tile * BN;
-    const auto rs = make_rsrc(vh + (size_t)kt * D, (uint32_t)(min(BN, a.Sk - kt) * D * 2));
-    const uint32_t dst = sV0 + (tile & 1) * (TILE * 2);
-#pragma unroll
-    for (int i = 0; i < BPW; ++i) dma16(rs, voff[i], dst + (i * (kThreads / 64) + wave) * 1024);
+    for (int i = 0; i < NBW - 1; ++i) dma16(disk[i] ? rk : rv, doff[i], (disk[i] ? kdst : vdst) + ddst[i]);
+    if (NB % 4 == 0 || nbw == NBW)
+      dma16(disk[NBW - 1] ? rk : rv, doff[NBW - 1], (disk[NBW - 1] ? kdst : vdst) + ddst[NBW - 1]);
   };
 
   // does every row of this wavefront see every key of tile t?
@@ -188,12 +217,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   };
 
   // Lane-constant byte offsets of the MFMA operand reads inside one LDS slot.
-  // The swizzles only depend on row bits that do not change between 32-key
-  // blocks, so block / step offsets become immediates of the ds_read.
-  uint32_t ka[NQK];
+  uint32_t ka[PAD ? 1 : NQK];
+  if constexpr (PAD) {
+    ka[0] = (uint32_t)(l32 * KS + 16 * hh);
+  } else {
 #pragma unroll
-  for (int t = 0; t < NQK; ++t)
-    ka[t] = (uint32_t)(l32 * D * 2 + (((2 * t + hh) ^ swz_k<D>(l32)) * 16));
+    for (int t = 0; t < NQK; ++t)
+      ka[t] = (uint32_t)(l32 * D * 2 + (((2 * t + hh) ^ swz_k<D>(l32)) * 16));
+  }
   const int vr0 = 8 * hh + ((lane & 15) >> 2);
   const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   uint32_t va[2][2][NDB];
@@ -204,18 +235,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const int row = 16 * s2 + vr0 + 4 * r2, col = 32 * db + vcol;
-        va[s2][r2][db] = (uint32_t)(row * D * 2 + (((col >> 3) ^ swz_v<D>(row)) * 16) + (col & 7) * 2);
+        if constexpr (PAD)
+          va[s2][r2][db] = (uint32_t)(row * VS + col * 2);
+        else
+          va[s2][r2][db] = (uint32_t)(row * D * 2 + (((col >> 3) ^ swz_v<D>(row)) * 16) + (col & 7) * 2);
       }
 
   auto qk = [&](int slot, f32x16* st) {
-    const char* kb_base = (const char*)&sK[0][0] + slot * (TILE * 2);
+    const char* kb_base = sK + slot * KSLOT;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) st[kb] = f32x16{};
 #pragma unroll
     for (int t = 0; t < NQK; ++t) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 kf = *(const bf16x8*)(kb_base + ka[t] + kb * 32 * D * 2);
+        const bf16x8 kf = PAD ? *(const bf16x8*)(kb_base + ka[0] + kb * 32 * KS + 32 * t)
+                              : *(const bf16x8*)(kb_base + ka[PAD ? 0 : t] + kb * 32 * D * 2);
         st[kb] = mfma32(kf, qf[t], st[kb]);
       }
     }
@@ -264,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
-    mx = fmaxf(mx, xor_shfl(mx, 32)) * c2;
+    mx = max_swap32(mx) * c2;
     if (__any(mx > m_run + kSlack)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
@@ -288,14 +323,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 
     // O^T += V^T P^T; the V^T operand for (db, kb, s) is two transposing
     // reads of keys 32kb + 16s + 8hh + [0..3] and [4..7], dims 32db + l32.
-    const char* vb = (const char*)&sV[0][0] + slot * (TILE * 2);
+    const char* vb = sV + slot * VSLOT;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const char* p0 = vb + kb * 32 * D * 2;
+          const char* p0 = vb + kb * 32 * (PAD ? VS : D * 2);
           const s16x4 lo4 = lds_read_tr16((const uint16_t*)(p0 + va[s2][0][db]));
           const s16x4 hi4 = lds_read_tr16((const uint16_t*)(p0 + va[s2][1][db]));
           const bf16x8 vf = __builtin_bit_cast(
@@ -309,17 +344,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   // K(t) and V(t) land in slot t&1; the loads of tile t+1 are issued as soon
   // as every wavefront is done with tile t-1 (the barrier), so they fly while
   // tile t is multiplied.
-  if (t_begin < t_end) {
-    issue_k(t_begin);
-    issue_v(t_begin);
-  }
+  if (t_begin < t_end) issue(t_begin);
   for (int tile = t_begin; tile < t_end; ++tile) {
     wait_vmcnt<0>();
     __syncthreads();
-    if (tile + 1 < t_end) {
-      issue_k(tile + 1);
-      issue_v(tile + 1);
-    }
+    if (tile + 1 < t_end) issue(tile + 1);
     {
       // a tile no row of this wavefront can see is masked to zero weight
       f32x16 st[NKB];
@@ -329,7 +358,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   }
 
   // ---- epilogue: normalise, round once to bf16, write o and lse ----------
-  const float l_tot = l_run + xor_shfl(l_run, 32);
+  const float l_tot = sum_swap32(l_run);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   if (q_ok) {
     uint16_t* orow = a.o + (q_base + qi) * D;
