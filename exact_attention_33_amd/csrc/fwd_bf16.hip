@@ -28,10 +28,10 @@
 //     the 8 keys a lane holds for each 16-key step consecutive.
 //   * two workgroups share each CU (one wavefront of each per SIMD) and are
 //     not coupled by barriers, so one wavefront's softmax overlaps the other's
-//     matrix-core work.  The tile loop body is branch-free apart from the
-//     rare wave-uniform rescale (a tile no row of the wavefront can see is
-//     simply masked to zero weight), which keeps the accumulators in place:
-//     no register copies at control-flow joins.
+//     matrix-core work.  Apart from the rare wave-uniform rescale, the only
+//     branch in the tile loop skips the matrix work of a tile no row of the
+//     wavefront can see (past the causal diagonal, outside the window); the
+//     accumulators keep one register home across it.
 //   * the running max is only raised when a row's new maximum exceeds it by
 //     more than kSlack (base-2 units); otherwise probabilities are taken
 //     against the old reference (bounded by 2^kSlack), which skips most
@@ -349,8 +349,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     wait_vmcnt<0>();
     __syncthreads();
     if (tile + 1 < t_end) issue(tile + 1);
-    {
-      // a tile no row of this wavefront can see is masked to zero weight
+    // skip the matrix work of a tile no row of this wavefront can see
+    const int kt0 = tile * BN, kt1 = kt0 + BN - 1;
+    bool any = kt0 < a.Sk;
+    if (a.causal) any = any && (kt0 <= phi);
+    if (w >= 0) any = any && (kt0 <= phi + w) && (kt1 >= plo - w);
+    if (any) {
       f32x16 st[NKB];
       qk(tile & 1, st);
       softmax_pv(tile & 1, tile, st);
