@@ -28,6 +28,12 @@ What it computes, and where the pages state it:
   LLM context, point 1) is a window; causal and GQA are readings stated in
   ``attention.py``.
 
+* ``attention_backward`` (``backward.py``) -- the gradients dq, dk, dv of
+  ``sum(do * attention(q, k, v))``: the derivative of the definition above,
+  written out by the chain rule (the pages name training as a use but print
+  no backward algorithm).  Pinned by tests/pins_backward.py (central finite
+  differences of ``attention``, torch autograd, closed-form special cases).
+
 Every function is fp64 throughout.  Parity pins: see tests/test_oracle_pins.py
 (brute force, online == two-pass, split+tree == unsplit, uniform scores,
 permutation invariance, special cases, overflow safety, GQA == MHA, the
@@ -47,3 +53,4 @@ from .attention import (  # noqa: F401
     finish,
     n_visible,
 )
+from .backward import attention_backward  # noqa: F401
