@@ -160,6 +160,25 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
                                       stream));
 }
 
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq, int Hkv,
+             int Sq, int Sk, int D, int causal, int window, float scale, hipStream_t stream) {
+  int st = check_fwd(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, window, scale);
+  if (st != ATTN_OK) return st;
+  const int64_t rows = (int64_t)B * Hq * Sq, keys = (int64_t)B * Hkv * Sk;
+  if (rows == 0 && keys == 0) return ATTN_OK;
+  if (rows > 0 && (q == nullptr || o == nullptr || dout == nullptr || lse == nullptr ||
+                   dq == nullptr || delta == nullptr))
+    return ATTN_ERR_NULL;
+  if (keys > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
+    return ATTN_ERR_NULL;
+  if (((int64_t)Sk + 127) / 128 * B * Hkv > INT32_MAX) return ATTN_ERR_SHAPE;  // grid size
+  return to_status(ea::launch_bwd((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                  (const uint16_t*)o, (const uint16_t*)dout, lse, (uint16_t*)dq,
+                                  (uint16_t*)dk, (uint16_t*)dv, delta,
+                                  fwd_shape(B, Hq, Hkv, Sq, Sk, D, causal, window, scale), stream));
+}
+
 int attn_decode_ex(const void* q, const void* kcache, const void* vcache, void* o, float* lse,
                    int B, int Hq, int Hkv, int Sk, int D, int num_splits, float scale,
                    void* workspace, size_t workspace_bytes, hipStream_t stream) {

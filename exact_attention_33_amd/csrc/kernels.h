@@ -22,6 +22,11 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                           const FwdShape& s, hipStream_t stream);
 
+// Backward: dq (and delta = rowsum(dout * o)), then dk and dv; two launches.
+hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                      const uint16_t* dout, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                      float* delta, const FwdShape& s, hipStream_t stream);
+
 struct DecodeShape {
   int B, Hq, Hkv, Sk, D, num_splits;
   float scale;

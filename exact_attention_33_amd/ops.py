@@ -23,7 +23,7 @@ STATUS_NAMES = {
     7: "ATTN_ERR_WORKSPACE", 8: "ATTN_ERR_HIP", 9: "ATTN_ERR_ARG",
 }
 # every symbol include/attn.h declares
-EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_decode", "attn_decode_ex",
+EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_bwd", "attn_decode", "attn_decode_ex",
            "attn_decode_workspace_bytes", "attn_error_string", "attn_version")
 
 _lib = None
@@ -49,6 +49,8 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd.restype = i
     L.attn_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
     L.attn_fwd_f32.restype = i
+    L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
+    L.attn_bwd.restype = i
     L.attn_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp]
     L.attn_decode.restype = i
     L.attn_decode_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
@@ -130,6 +132,43 @@ def attn_fwd(q, k, v, causal=False, window=-1, scale=None, out=None, lse=None, r
 def attn_fwd_f32(q, k, v, causal=False, window=-1, scale=None, out=None, lse=None, return_lse=True):
     """Prefill on fp32 tensors (no bf16 rounding anywhere) -> ``(o, lse)``."""
     return _fwd(lib().attn_fwd_f32, torch.float32, q, k, v, causal, window, scale, out, lse, return_lse)
+
+
+def attn_bwd(q, k, v, o, dout, lse, causal=False, window=-1, scale=None, dq=None, dk=None, dv=None,
+             delta=None):
+    """Gradients of ``sum(dout * o)`` for the bf16 prefill -> ``(dq, dk, dv)``.
+
+    ``o`` and ``lse`` are the forward's outputs for the same inputs and mask;
+    ``delta`` (fp32 ``[B, Hq, Sq]``) is scratch, allocated here if not given.
+    """
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be on a GPU")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _want(t, n, torch.bfloat16, 4, dev)
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, Sk, Dk = k.shape
+    if v.shape != k.shape or Bk != B or Dk != D or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("shape mismatch between q, k, v, o, dout")
+    _want(lse, "lse", torch.float32, 3, dev)
+    if tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("lse must be [B, Hq, Sq]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    delta = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev) if delta is None else delta
+    for t, n, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        _want(t, n, torch.bfloat16, 4, dev)
+        if t.shape != ref.shape:
+            raise ValueError(f"{n} must have the shape of its input")
+    _want(delta, "delta", torch.float32, 3, dev)
+    if tuple(delta.shape) != (B, Hq, Sq):
+        raise ValueError("delta must be [B, Hq, Sq]")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                          _ptr(dv), _ptr(delta), B, Hq, Hkv, Sq, Sk, D, int(causal), int(window), scale,
+                          _stream(q)))
+    return dq, dk, dv
 
 
 def _decode_shapes(q, kcache, vcache, out):

@@ -49,6 +49,14 @@ def draw_qkv(q_shape, kv_shape, dtype: str, seed: int, device="cpu"):
     return q, k, v
 
 
+def draw_grad(shape, dtype: str, seed: int, device="cpu"):
+    """An upstream gradient ~ N(0,1) from its own seeded generator (seed + 7919),
+    rounded to ``dtype``."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) + 7919)
+    return torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(TORCH_DTYPES[dtype])
+
+
 def workload_inputs(name: str, device="cpu", seed: int | None = None):
     """Inputs of a named workload: dict with q, k, v and the call parameters."""
     w = dict(WORKLOADS[name])

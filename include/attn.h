@@ -83,6 +83,33 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
                  int causal, int window, float scale, hipStream_t stream);
 
 /*
+ * Backward of attn_fwd (bf16): the gradients of sum(dout * o) with respect to
+ * q, k and v, with o = softmax(scale * q k^T) v under the same causal /
+ * window / GQA rules.  The pages name training as a use of the fused method
+ * (FlashAttention explainer, "Overview"; FlashAttention-3 article, "Benefits
+ * of FlashAttention-3") but print no backward algorithm; this computes the
+ * derivative of the forward definition:
+ *   P = exp(scale q k^T - lse), dv = P^T dout, dP = dout v^T,
+ *   delta = rowsum(dout * o), dS = P * (dP - delta),
+ *   dq = scale dS k, dk = scale dS^T q  (dk, dv summed over a GQA group).
+ * The probabilities are recomputed from the forward's lse; nothing of size
+ * Sq x Sk is stored.
+ *
+ *   q, o, dout, dq : bf16 [B, Hq, Sq, D].   k, v, dk, dv: bf16 [B, Hkv, Sk, D].
+ *   lse            : fp32 [B, Hq, Sq], as written by attn_fwd for the same
+ *                    q, k, v and mask (-inf for rows with no visible key).
+ *   delta          : caller-owned fp32 scratch of B*Hq*Sq floats; on return it
+ *                    holds rowsum(dout * o).
+ * Rows or keys that see nothing get zero gradients.  Two launches on `stream`
+ * (dq and delta, then dk and dv).  Same validation and errors as attn_fwd;
+ * ATTN_ERR_NULL if any pointer needed for a non-empty output is NULL.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, float* delta,
+             int B, int Hq, int Hkv, int Sq, int Sk, int D,
+             int causal, int window, float scale, hipStream_t stream);
+
+/*
  * Single-token decode against a KV cache, bf16, scale = 1/sqrt(D), split-KV.
  *
  *   q, o           : bf16 [B, Hq, D].   kcache, vcache: bf16 [B, Hkv, Sk, D].
