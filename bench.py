@@ -198,7 +198,35 @@ def other_configs(dev, iters: int = 20):
                 "algorithmic_bytes": kv,
             }
         del ev
-    del ww, wl, o, od, ws
+    # backward of the causal prefill (dq, dk, dv from the forward's o and lse)
+    wp = synth.workload_inputs(PREFILL, dev)
+    do = synth.draw_grad(wp["q"].shape, "bf16", wp["seed"], dev)
+    op, lp = ops.attn_fwd(wp["q"], wp["k"], wp["v"], causal=True, scale=wp["scale"])
+    dq, dk, dv = torch.empty_like(wp["q"]), torch.empty_like(wp["k"]), torch.empty_like(wp["v"])
+    delta = torch.empty_like(lp)
+
+    def run_b():
+        ops.attn_bwd(wp["q"], wp["k"], wp["v"], op, do, lp, causal=True, scale=wp["scale"], dq=dq, dk=dk,
+                     dv=dv, delta=delta)
+
+    for _ in range(10):
+        run_b()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(iters)]
+    for i in range(iters):
+        ev[i][0].record(stream)
+        run_b()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / iters
+    fl = 2.5 * prefill_flops(wp)   # five products of the forward's size: S, dP, dV, dK, dQ
+    out["causal_prefill_backward"] = {
+        "shape": {k: wp[k] for k in ("B", "Hq", "Hkv", "Sq", "D")}, "avg_launch_ms": round(ms, 5),
+        "bound": "mfma", "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+        "frac_of_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "algorithmic_flops": fl,
+        "note": "dq kernel + dk/dv kernel; algorithmic work counts S, dP, dV, dK, dQ once (the kernels "
+                "recompute S and dP in both passes)",
+    }
+    del ww, wl, o, od, ws, wp, do, op, lp, dq, dk, dv, delta
     torch.cuda.empty_cache()
     return out
 

@@ -25,6 +25,8 @@
 //     from LDS, B = the wavefront's keys), a lane holding one key; then
 //     dv^T += dout^T P and dk^T += q^T dS.  The group's query heads are summed
 //     in registers, so no atomics are needed.
+// Both kernels run two wavefronts per SIMD (two workgroups per CU), so one
+// wavefront's softmax-side vector work overlaps the other's matrix work.
 // The A-operand rows of S / S^T and dP / dP^T are read with bits 2 and 3 of
 // the row index swapped; the 8 values a lane then holds for each 16-row
 // MFMA step are consecutive rows, which is the B-operand layout of the
@@ -243,7 +245,7 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dq_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreadsB, 2) void bwd_dkdv_kernel(BwdArgs a) {
   using G = TileGeo<D>;
   constexpr int NQK = D / 16;
   constexpr int NDB = D / 32;
