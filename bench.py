@@ -198,6 +198,33 @@ def other_configs(dev, iters: int = 20):
                 "algorithmic_bytes": kv,
             }
         del ev
+    # encoder stack pattern at the window-encoder shape: a global (unmasked)
+    # layer every third layer, windowed layers otherwise (no new kernel)
+    og = torch.empty_like(ww["q"])
+
+    def run_g():
+        ops.attn_fwd(ww["q"], ww["k"], ww["v"], causal=False, window=-1, scale=ww["scale"], out=og, lse=lse)
+
+    for _ in range(3):
+        run_g()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
+    for i in range(5):
+        ev[i][0].record(stream)
+        run_g()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    g_ms = sum(a.elapsed_time(b) for a, b in ev) / 5
+    S, D_ = ww["Sq"], ww["D"]
+    g_fl = 4.0 * D_ * S * S * ww["B"] * ww["Hq"]
+    l_ms = out["window_encoder"]["avg_launch_ms"]
+    out["encoder_stack"] = {
+        "pattern": "one global layer (window -1) then two local layers (window 64), ModernBERT-style",
+        "shape": {k: ww[k] for k in ("B", "Hq", "Sq", "D")},
+        "global_layer_ms": round(g_ms, 4), "global_layer_tflops": round(g_fl / (g_ms * 1e-3) / 1e12, 1),
+        "local_layer_ms": l_ms, "three_layer_attention_ms": round(g_ms + 2 * l_ms, 4),
+    }
+    del og
+
     # backward of the causal prefill (dq, dk, dv from the forward's o and lse)
     wp = synth.workload_inputs(PREFILL, dev)
     do = synth.draw_grad(wp["q"].shape, "bf16", wp["seed"], dev)

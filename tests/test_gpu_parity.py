@@ -264,3 +264,27 @@ def test_runs_on_the_callers_stream():
         o, _ = ops.attn_fwd(q, k, v)
     s.synchronize()
     assert torch.equal(o, ref)
+
+
+# --------------------------------------------------------------------------
+# Encoder stack pattern: the global layer of the window-encoder shape
+# --------------------------------------------------------------------------
+
+def test_encoder_global_layer_sampled_rows():
+    """Full attention (no mask) at the window-encoder shape B8 H12 S8192 D64,
+    the global layer that the local/global encoder pattern interleaves with
+    the windowed one; checked on sampled rows (the oracle computes them one
+    by one), including the first and last rows."""
+    w = synth.WORKLOADS["window_encoder"]
+    q, k, v = synth.draw_qkv((w["B"], w["Hq"], w["Sq"], w["D"]), (w["B"], w["Hkv"], w["Sk"], w["D"]), "bf16",
+                             synth.SEEDS["window_encoder"], DEV)
+    scale = synth.default_scale(w["D"])
+    announce("encoder global layer B8 H12 S8192 D64 (no mask), sampled rows")
+    o, lse = ops.attn_fwd(q, k, v, causal=False, window=-1, scale=scale)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 63, 64, 127, 128, 4095, 4096, 8190, 8191])
+    o_ref, lse_ref = oracle.attention(to_numpy_exact(q), to_numpy_exact(k), to_numpy_exact(v), scale, False, -1,
+                                      rows=rows)
+    e = check_o(o[:, :, rows], o_ref, "bf16", "global layer")
+    le = check_lse(lse[:, :, rows], lse_ref, "bf16", "global layer")
+    announce(f"global layer: {e} lse_err {le:.3g}")
