@@ -12,8 +12,8 @@
 //
 // Two kernels, launched in this order on one stream:
 //   * bwd_dq_kernel: one workgroup = 4 wavefronts x 32 query rows of one
-//     (b, h).  q and dout stay in registers; K/V tiles of 32 keys stream
-//     through LDS.  Per tile and wavefront: S^T = K q^T and dP^T = V dout^T
+//     (b, h).  q and dout stay in registers; K/V tiles of 64 keys (two
+//     32-key halves per barrier) stream through LDS.  Per tile and wavefront: S^T = K q^T and dP^T = V dout^T
 //     (A = 32 keys from LDS, B = the wavefront's 32 queries in registers),
 //     so a lane holds one query and its lse / delta are lane scalars; then
 //     dq^T += K^T dS^T with K^T read by the transposing LDS load.  It first
@@ -82,13 +82,13 @@ __device__ __forceinline__ uint32_t tile_src(int p) {
 
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreadsB, 1) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreadsB, 2) void bwd_dq_kernel(BwdArgs a) {
   using G = TileGeo<D>;
   constexpr int NQK = D / 16;    // k-steps over dims
   constexpr int NDB = D / 32;    // 32-dim blocks of dq^T
-  constexpr int NB2 = 2 * G::BLK;                 // blocks of a (K, V) stage
-  constexpr int NBW = (NB2 + 3) / 4;
-  __shared__ __attribute__((aligned(1024))) char sT[2][2 * G::BYTES];   // [stage][K | V]
+  // a stage holds 64 keys as four padded 32-row tiles: K0 | K1 | V0 | V1;
+  // wavefront w loads tile w
+  __shared__ __attribute__((aligned(1024))) char sT[2][4 * G::BYTES];
 
   const int BH = a.B * a.Hq;
   const int bh = blockIdx.x % BH, qtile = blockIdx.x / BH;
@@ -108,8 +108,8 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dq_kernel(BwdArgs a) {
     kv_lo = max(kv_lo, r0 + off - w);
     kv_hi = min(kv_hi, r1 + off + w + 1);
   }
-  const int t_begin = max(kv_lo, 0) / 32;
-  const int t_end = (kv_hi > kv_lo) ? (kv_hi + 31) / 32 : t_begin;
+  const int t_begin = max(kv_lo, 0) / 64;
+  const int t_end = (kv_hi > kv_lo) ? (kv_hi + 63) / 64 : t_begin;
 
   const size_t q_base = ((size_t)b * a.Hq + h) * (size_t)a.Sq;
   const size_t kv_base = ((size_t)b * a.Hkv + g) * (size_t)a.Sk;
@@ -153,27 +153,20 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dq_kernel(BwdArgs a) {
   }
   if (!q_ok) key_hi = -1;
 
-  // tile loads: (K, V) stage, blocks i*4 + wave
-  uint32_t doff[NBW], ddst[NBW];
-  bool disk[NBW];
+  // tile loads: wavefront w fills tile w of the stage (K0, K1, V0, V1)
+  uint32_t doff[G::BLK];
 #pragma unroll
-  for (int i = 0; i < NBW; ++i) {
-    const int bb = i * 4 + wave;
-    disk[i] = bb < G::BLK;
-    const int tb = disk[i] ? bb : bb - G::BLK;
-    doff[i] = tile_src<D>(tb * 64 + lane);
-    ddst[i] = (uint32_t)(bb * 1024);
-  }
+  for (int i = 0; i < G::BLK; ++i) doff[i] = tile_src<D>(i * 64 + lane);
+  const uint16_t* src_base = (wave < 2) ? kh : vh;
+  const int src_half = (wave & 1) * 32;
   const uint32_t sT0 = lds_addr(&sT[0][0]);
   auto issue = [&](int tile, int st) {
-    const int kt = tile * 32;
-    const uint32_t bytes = (uint32_t)(min(32, a.Sk - kt) * D * 2);
-    const auto rk = make_rsrc(kh + (size_t)kt * D, bytes);
-    const auto rv = make_rsrc(vh + (size_t)kt * D, bytes);
-    const uint32_t base = sT0 + st * (2 * G::BYTES);
+    const int kt = tile * 64 + src_half;
+    const int rows = max(0, min(32, a.Sk - kt));
+    const auto rs = make_rsrc(src_base + (size_t)(rows > 0 ? kt : 0) * D, (uint32_t)(rows * D * 2));
+    const uint32_t base = sT0 + st * (4 * G::BYTES) + wave * G::BYTES;
 #pragma unroll
-    for (int i = 0; i < NBW; ++i)
-      if (i * 4 + wave < NB2) dma16(disk[i] ? rk : rv, doff[i], base + ddst[i]);
+    for (int i = 0; i < G::BLK; ++i) dma16(rs, doff[i], base + i * 1024);
   };
 
   // lane bases of the operand reads inside one tile
@@ -193,8 +186,10 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dq_kernel(BwdArgs a) {
     wait_vmcnt<0>();
     __syncthreads();
     if (tile + 1 < t_end) issue(tile + 1, st ^ 1);
-    const char* kb = &sT[st][0];
-    const char* vb = &sT[st][G::BYTES];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+    const char* kb = &sT[st][j * G::BYTES];
+    const char* vb = &sT[st][(2 + j) * G::BYTES];
 
     // S^T = K q^T, dP^T = V dout^T (32 keys x 32 queries each)
     f32x16 s = f32x16{}, dp = f32x16{};
@@ -206,7 +201,7 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dq_kernel(BwdArgs a) {
       dp = mfma32(va, df[t], dp);
     }
     // element r holds key kt0 + 16*(r/8) + 8*hh + r%8 of this lane's query
-    const int kt0 = tile * 32;
+    const int kt0 = tile * 64 + 32 * j;
     const int lo = key_lo - kt0 - 8 * hh, hi = key_hi - kt0 - 8 * hh;
     bf16x8 dsb[2];
 #pragma unroll
@@ -227,6 +222,7 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dq_kernel(BwdArgs a) {
         const bf16x8 kt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[db] = mfma32(kt, dsb[s2], acc[db]);
       }
+    }
   }
 
   if (q_ok) {
