@@ -8,11 +8,15 @@ kernel is measured in its steady state; the same steps run interleaved are
 reported alongside ("interleaved").
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --only WORKLOAD [--steps K] [--warmup W]   (one workload, for profilers)
 
 Prints ONE JSON line.  `value` is the mean of the two roofline fractions, in
 percent: prefill TFLOP/s over the dense bf16 MFMA peak and decode KV GB/s over
 the HBM peak.  Per-call durations come from HIP events recorded on the stream
-the kernels are launched on, inside the timed region.
+the kernels are launched on, inside the timed region; each series is reported
+with its mean, median and 10th/90th percentiles.  Two plain reference kernels
+built into the library (an HBM stream and an MFMA loop) give the achievable
+rates, and every rate is also stated as a fraction of those.
 """
 
 from __future__ import annotations
@@ -34,7 +38,7 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 
 PREFILL = "causal_prefill"
 DECODE = "gqa_decode"
-KERNEL_SOURCES = ["fwd_bf16.hip", "decode.hip", "common.h"]
+KERNEL_SOURCES = ["fwd_bf16.hip", "decode.hip", "bwd.hip", "common.h"]
 
 
 def visible_pairs_causal(Sq: int, Sk: int) -> int:
@@ -50,6 +54,75 @@ def prefill_flops(w) -> float:
 
 def decode_kv_bytes(w) -> float:
     return 2.0 * w["B"] * w["Hkv"] * w["Sk"] * w["D"] * 2
+
+
+def launch_stats(ms):
+    """Mean, median and 10th/90th percentiles of per-launch durations (ms)."""
+    v = sorted(ms)
+    n = len(v)
+
+    def pct(p):
+        return v[min(n - 1, int(round(p * (n - 1))))]
+
+    return {"n": n, "avg_ms": round(sum(v) / n, 5), "median_ms": round(pct(0.5), 5),
+            "p10_ms": round(pct(0.1), 5), "p90_ms": round(pct(0.9), 5)}
+
+
+def time_launches(fn, iters: int, stream, warm: int = 10):
+    """Per-launch durations (ms) of fn(i), HIP events recorded on `stream`."""
+    import torch
+
+    for i in range(warm):
+        fn(i)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(iters)]
+    for i in range(iters):
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def scores_bytes_avoided(B: int, Hq: int, Sq: int, Sk: int) -> float:
+    """HBM bytes of the Sq x Sk score matrix that standard attention moves and the
+    fused kernels never do: S written and read back, P written and read back (bf16)."""
+    return 4.0 * 2 * B * Hq * Sq * Sk
+
+
+def achievable(dev):
+    """Rates of the library's plain reference kernels on this GPU: an HBM read
+    stream, a 3-read/1-write stream (the prefill's q, k, v -> o mix) and a bf16
+    MFMA loop.  Each is the median of several launches after a warm-up."""
+    import torch
+
+    from exact_attention_33_amd import ops
+
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    mib = 1 << 20
+    src = torch.empty(2048 * mib, dtype=torch.uint8, device=dev)
+    dst = torch.empty(8 * mib, dtype=torch.uint8, device=dev)
+    ms = launch_stats(time_launches(lambda i: ops.calib_stream(src, dst), 10, stream, warm=5))["median_ms"]
+    out["hbm_read_gbs"] = round((src.numel() + dst.numel()) / (ms * 1e-3) / 1e9, 1)
+    del src, dst
+    src = torch.empty(3 * 256 * mib, dtype=torch.uint8, device=dev)
+    dst = torch.empty(256 * mib, dtype=torch.uint8, device=dev)
+    ms = launch_stats(time_launches(lambda i: ops.calib_stream(src, dst), 10, stream, warm=5))["median_ms"]
+    out["hbm_3read_1write_gbs"] = round((src.numel() + dst.numel()) / (ms * 1e-3) / 1e9, 1)
+    del src, dst
+    wg, iters = 2048, 4000
+    o = torch.empty(4 * wg, dtype=torch.float32, device=dev)
+    flops = [0.0]
+
+    def run(i):
+        flops[0] = ops.calib_mfma(o, wg, iters)
+
+    ms = launch_stats(time_launches(run, 10, stream, warm=5))["median_ms"]
+    out["mfma_bf16_tflops"] = round(flops[0] / (ms * 1e-3) / 1e12, 1)
+    out["note"] = ("attn_calib_stream over 2 GiB (read) and 3 x 256 MiB -> 256 MiB (3:1); attn_calib_mfma: "
+                   f"{wg} workgroups x 4 wavefronts x {iters} x 4 v_mfma_f32_32x32x16_bf16")
+    torch.cuda.empty_cache()
+    return out
 
 
 def source_digest() -> str:
@@ -74,6 +147,17 @@ def measured_traffic(kind: str):
     return entry.get("bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(budget_s: float = 20.0):
     """The fp64 oracle, untuned, on a bounded sample of the same workloads."""
     import numpy as np
@@ -84,8 +168,8 @@ def cpu_baseline(budget_s: float = 20.0):
 
     try:
         from threadpoolctl import threadpool_info
-        blas = [(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info()]
-        threads = max([n for _, n in blas if n] or [1])
+        blas = [(i.get("internal_api"), i.get("version"), i.get("num_threads")) for i in threadpool_info()]
+        threads = max([n for _, _, n in blas if n] or [1])
     except Exception:  # noqa: BLE001
         blas, threads = [], 1
     wp = synth.WORKLOADS[PREFILL]
@@ -123,7 +207,7 @@ def cpu_baseline(budget_s: float = 20.0):
                    f"{tp:.2f} s -> {tflops * 1e3:.2f} GFLOP/s; decode on {nb} of 16 batch rows "
                    f"(Hq=32, Hkv=8, Sk=32768) took {td:.2f} s -> {gbs:.2f} GB/s of bf16 KV"),
         "prefill_gflops": tflops * 1e3, "decode_gbs": gbs,
-        "affinity_cores": len(os.sched_getaffinity(0)), "blas": blas,
+        "affinity_cores": len(os.sched_getaffinity(0)), "blas": blas, "cpu_model": cpu_model(),
     }
 
 
@@ -139,21 +223,61 @@ def window_flops(w) -> float:
     return 4.0 * w["D"] * pairs * w["B"] * w["Hq"]
 
 
-def other_configs(dev, iters: int = 20):
-    """The sliding-window encoder and the long-context decode at full size,
-    timed warm with HIP events (reported beside the headline, not in it)."""
+def other_configs(dev, ach, iters: int = 50):
+    """The sliding-window encoder, the long-context decode, the encoder-stack
+    pattern and the causal-prefill backward at full size, timed with HIP events
+    (reported beside the headline, not in it).  The window encoder's inputs
+    and outputs (402 MB) would otherwise sit in the 256 MB last-level cache
+    between launches, so launches rotate over three copies of them."""
     import torch
 
     from exact_attention_33_amd import ops, synth
 
     out = {}
+    stream = torch.cuda.current_stream(dev)
     ww = synth.workload_inputs("window_encoder", dev)
-    o = torch.empty_like(ww["q"])
-    lse = torch.empty(ww["B"], ww["Hq"], ww["Sq"], dtype=torch.float32, device=dev)
+    copies = []
+    for c in range(3):
+        q, k, v = (ww[n] if c == 0 else ww[n].clone() for n in ("q", "k", "v"))
+        copies.append((q, k, v, torch.empty_like(q),
+                       torch.empty(ww["B"], ww["Hq"], ww["Sq"], dtype=torch.float32, device=dev)))
 
-    def run_w():
-        ops.attn_fwd(ww["q"], ww["k"], ww["v"], causal=False, window=ww["window"], scale=ww["scale"],
-                     out=o, lse=lse)
+    def run_w(i, window=ww["window"]):
+        q, k, v, o, lse = copies[i % 3]
+        ops.attn_fwd(q, k, v, causal=False, window=window, scale=ww["scale"], out=o, lse=lse)
+
+    st = launch_stats(time_launches(run_w, iters, stream))
+    ms = st["avg_ms"]
+    nbytes = window_bytes(ww)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out["window_encoder"] = {
+        "shape": {k: ww[k] for k in ("B", "Hq", "Sq", "D", "window")},
+        "avg_launch_ms": ms, "launch_ms": st,
+        "bound": "hbm", "achieved_gbs": round(gbs, 1),
+        "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "frac_of_achievable": round(gbs / ach["hbm_3read_1write_gbs"], 4),
+        "algorithmic_bytes": nbytes, "traffic": measured_traffic("window_encoder"),
+        "tflops": round(window_flops(ww) / (ms * 1e-3) / 1e12, 1),
+        "scores_bytes_avoided": scores_bytes_avoided(ww["B"], ww["Hq"], ww["Sq"], ww["Sq"]),
+        "inputs": "three copies of q, k, v, o, lse, rotated per launch",
+    }
+
+    # encoder stack pattern at the window-encoder shape: a global (unmasked)
+    # layer every third layer, windowed layers otherwise (no new kernel)
+    stg = launch_stats(time_launches(lambda i: run_w(i, window=-1), 10, stream, warm=3))
+    g_ms = stg["avg_ms"]
+    S, D_ = ww["Sq"], ww["D"]
+    g_fl = 4.0 * D_ * S * S * ww["B"] * ww["Hq"]
+    out["encoder_stack"] = {
+        "pattern": "one global layer (window -1) then two local layers (window 64), ModernBERT-style",
+        "shape": {k: ww[k] for k in ("B", "Hq", "Sq", "D")},
+        "global_layer_ms": g_ms, "global_launch_ms": stg,
+        "global_layer_tflops": round(g_fl / (g_ms * 1e-3) / 1e12, 1),
+        "global_frac_of_achievable_mfma": round(g_fl / (g_ms * 1e-3) / 1e12 / ach["mfma_bf16_tflops"], 4),
+        "local_layer_ms": ms, "three_layer_attention_ms": round(g_ms + 2 * ms, 4),
+        "global_traffic": measured_traffic("global_layer"),
+    }
+    del copies, ww
 
     wl = synth.workload_inputs("long_decode", dev)
     od = torch.empty_like(wl["q"])
@@ -161,69 +285,24 @@ def other_configs(dev, iters: int = 20):
     ws = torch.empty(ops.decode_workspace_bytes(wl["B"], wl["Hq"], wl["D"], wl["num_splits"]),
                      dtype=torch.uint8, device=dev)
 
-    def run_l():
+    def run_l(i):
         ops.attn_decode_ex(wl["q"], wl["k"], wl["v"], wl["num_splits"], scale=wl["scale"], out=od,
                            lse=lsed, workspace=ws)
 
-    stream = torch.cuda.current_stream(dev)
-    for name, fn in (("window_encoder", run_w), ("long_decode", run_l)):
-        for _ in range(10):
-            fn()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(iters)]
-        for i in range(iters):
-            ev[i][0].record(stream)
-            fn()
-            ev[i][1].record(stream)
-        torch.cuda.synchronize()
-        ms = sum(a.elapsed_time(b) for a, b in ev) / iters
-        if name == "window_encoder":
-            w = ww
-            nbytes = window_bytes(w)
-            out[name] = {
-                "shape": {k: w[k] for k in ("B", "Hq", "Sq", "D", "window")},
-                "avg_launch_ms": round(ms, 5),
-                "bound": "hbm", "achieved_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                "algorithmic_bytes": nbytes,
-                "tflops": round(window_flops(w) / (ms * 1e-3) / 1e12, 1),
-            }
-        else:
-            w = wl
-            kv = decode_kv_bytes(w)
-            out[name] = {
-                "shape": {k: w[k] for k in ("B", "Hq", "Hkv", "Sk", "D", "num_splits")},
-                "avg_launch_ms": round(ms, 5),
-                "bound": "hbm", "achieved_gbs": round(kv / (ms * 1e-3) / 1e9, 1),
-                "frac_of_hbm_peak": round(kv / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                "algorithmic_bytes": kv,
-            }
-        del ev
-    # encoder stack pattern at the window-encoder shape: a global (unmasked)
-    # layer every third layer, windowed layers otherwise (no new kernel)
-    og = torch.empty_like(ww["q"])
-
-    def run_g():
-        ops.attn_fwd(ww["q"], ww["k"], ww["v"], causal=False, window=-1, scale=ww["scale"], out=og, lse=lse)
-
-    for _ in range(3):
-        run_g()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
-    for i in range(5):
-        ev[i][0].record(stream)
-        run_g()
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    g_ms = sum(a.elapsed_time(b) for a, b in ev) / 5
-    S, D_ = ww["Sq"], ww["D"]
-    g_fl = 4.0 * D_ * S * S * ww["B"] * ww["Hq"]
-    l_ms = out["window_encoder"]["avg_launch_ms"]
-    out["encoder_stack"] = {
-        "pattern": "one global layer (window -1) then two local layers (window 64), ModernBERT-style",
-        "shape": {k: ww[k] for k in ("B", "Hq", "Sq", "D")},
-        "global_layer_ms": round(g_ms, 4), "global_layer_tflops": round(g_fl / (g_ms * 1e-3) / 1e12, 1),
-        "local_layer_ms": l_ms, "three_layer_attention_ms": round(g_ms + 2 * l_ms, 4),
+    st = launch_stats(time_launches(run_l, 20, stream))
+    ms = st["avg_ms"]
+    kv = decode_kv_bytes(wl)
+    gbs = kv / (ms * 1e-3) / 1e9
+    out["long_decode"] = {
+        "shape": {k: wl[k] for k in ("B", "Hq", "Hkv", "Sk", "D", "num_splits")},
+        "avg_launch_ms": ms, "launch_ms": st,
+        "bound": "hbm", "achieved_gbs": round(gbs, 1),
+        "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "frac_of_achievable": round(gbs / ach["hbm_read_gbs"], 4),
+        "algorithmic_bytes": kv, "traffic": measured_traffic("long_decode"),
+        "scores_bytes_avoided": scores_bytes_avoided(wl["B"], wl["Hq"], 1, wl["Sk"]),
     }
-    del og
+    del wl, od, lsed, ws
 
     # backward of the causal prefill (dq, dk, dv from the forward's o and lse)
     wp = synth.workload_inputs(PREFILL, dev)
@@ -232,42 +311,89 @@ def other_configs(dev, iters: int = 20):
     dq, dk, dv = torch.empty_like(wp["q"]), torch.empty_like(wp["k"]), torch.empty_like(wp["v"])
     delta = torch.empty_like(lp)
 
-    def run_b():
+    def run_b(i):
         ops.attn_bwd(wp["q"], wp["k"], wp["v"], op, do, lp, causal=True, scale=wp["scale"], dq=dq, dk=dk,
                      dv=dv, delta=delta)
 
-    for _ in range(10):
-        run_b()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(iters)]
-    for i in range(iters):
-        ev[i][0].record(stream)
-        run_b()
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in ev) / iters
+    st = launch_stats(time_launches(run_b, iters, stream))
+    ms = st["avg_ms"]
     fl = 2.5 * prefill_flops(wp)   # five products of the forward's size: S, dP, dV, dK, dQ
+    tf = fl / (ms * 1e-3) / 1e12
     out["causal_prefill_backward"] = {
-        "shape": {k: wp[k] for k in ("B", "Hq", "Hkv", "Sq", "D")}, "avg_launch_ms": round(ms, 5),
-        "bound": "mfma", "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
-        "frac_of_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "algorithmic_flops": fl,
+        "shape": {k: wp[k] for k in ("B", "Hq", "Hkv", "Sq", "D")}, "avg_launch_ms": ms, "launch_ms": st,
+        "bound": "mfma", "tflops": round(tf, 1),
+        "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+        "frac_of_achievable": round(tf / ach["mfma_bf16_tflops"], 4), "algorithmic_flops": fl,
+        "traffic": measured_traffic("backward"),
         "note": "dq kernel + dk/dv kernel; algorithmic work counts S, dP, dV, dK, dQ once (the kernels "
                 "recompute S and dP in both passes)",
     }
-    del ww, wl, o, od, ws, wp, do, op, lp, dq, dk, dv, delta
+    del wp, do, op, lp, dq, dk, dv, delta
     torch.cuda.empty_cache()
     return out
+
+
+def run_only(name: str, steps: int, warmup: int, dev):
+    """Run one workload alone (warm-up, then `steps` timed launches) and print
+    its launch statistics: the command profilers wrap."""
+    import torch
+
+    from exact_attention_33_amd import ops, synth
+
+    stream = torch.cuda.current_stream(dev)
+    if name in ("causal_prefill", "window_encoder", "global_layer", "backward"):
+        w = synth.workload_inputs("window_encoder" if name == "global_layer" else
+                                  ("causal_prefill" if name == "backward" else name), dev)
+        window = -1 if name == "global_layer" else w["window"]
+        o = torch.empty_like(w["q"])
+        lse = torch.empty(w["B"], w["Hq"], w["Sq"], dtype=torch.float32, device=dev)
+        if name == "backward":
+            do = synth.draw_grad(w["q"].shape, "bf16", w["seed"], dev)
+            ops.attn_fwd(w["q"], w["k"], w["v"], causal=True, scale=w["scale"], out=o, lse=lse)
+            dq, dk, dv = torch.empty_like(w["q"]), torch.empty_like(w["k"]), torch.empty_like(w["v"])
+            delta = torch.empty_like(lse)
+
+            def fn(i):
+                ops.attn_bwd(w["q"], w["k"], w["v"], o, do, lse, causal=True, scale=w["scale"], dq=dq, dk=dk,
+                             dv=dv, delta=delta)
+        else:
+            # three rotated copies of the inputs and outputs, as in the full run
+            cp = [(w["q"], w["k"], w["v"], o, lse)] + [
+                (w["q"].clone(), w["k"].clone(), w["v"].clone(), torch.empty_like(o), torch.empty_like(lse))
+                for _ in range(2)]
+
+            def fn(i):
+                q, k, v, oo, ll = cp[i % 3]
+                ops.attn_fwd(q, k, v, causal=bool(w["causal"]), window=window, scale=w["scale"], out=oo, lse=ll)
+    elif name in ("gqa_decode", "long_decode"):
+        w = synth.workload_inputs(name, dev)
+        o = torch.empty_like(w["q"])
+        lse = torch.empty(w["B"], w["Hq"], dtype=torch.float32, device=dev)
+        ws = torch.empty(ops.decode_workspace_bytes(w["B"], w["Hq"], w["D"], w["num_splits"]),
+                         dtype=torch.uint8, device=dev)
+
+        def fn(i):
+            ops.attn_decode_ex(w["q"], w["k"], w["v"], w["num_splits"], scale=w["scale"], out=o, lse=lse,
+                               workspace=ws)
+    else:
+        raise SystemExit(f"unknown workload {name!r}")
+    st = launch_stats(time_launches(fn, steps, stream, warm=warmup))
+    print(json.dumps({"only": name, "launch_ms": st}), flush=True)
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=60,
                     help="untimed steps first; the GPU needs tens of milliseconds of work to reach its steady clock")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (three times), the known-size "
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--only", default=None,
+                    help="time one workload alone and print its launch statistics (for profilers): "
+                         "causal_prefill, window_encoder, global_layer, backward, gqa_decode, long_decode")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -287,6 +413,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": 1 << 30, "copies": 3}), flush=True)
+        return
+    if args.only:
+        run_only(args.only, args.steps, args.warmup, dev)
         return
     wp = synth.workload_inputs(PREFILL, dev)
     wd = synth.workload_inputs(DECODE, dev)
@@ -350,6 +479,7 @@ def main():
     ip_avg = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
     id_avg = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
 
+    ach = achievable(dev)
     flops = prefill_flops(wp)
     kv = decode_kv_bytes(wd)
     p_tflops = flops / (p_avg * 1e-3) / 1e12
@@ -376,14 +506,19 @@ def main():
             "kernel": "decode (split kernel + tree combine), the larger share of the step",
             "bound": "hbm", "achieved": round(d_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(d_frac, 4), "traffic": measured_traffic("decode"),
-            "algorithmic_bytes": kv, "avg_launch_ms": round(d_avg, 5),
+            "algorithmic_bytes": kv, "avg_launch_ms": round(d_avg, 5), "launch_ms": launch_stats(d_ms),
+            "frac_of_achievable": round(d_gbs / ach["hbm_read_gbs"], 4),
+            "scores_bytes_avoided": scores_bytes_avoided(wd["B"], wd["Hq"], 1, wd["Sk"]),
         },
         "roofline_prefill": {
             "kernel": "fwd_bf16 causal prefill",
             "bound": "mfma", "achieved": round(p_tflops, 1), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(p_frac, 4), "traffic": measured_traffic("prefill"),
-            "algorithmic_flops": flops, "avg_launch_ms": round(p_avg, 5),
+            "algorithmic_flops": flops, "avg_launch_ms": round(p_avg, 5), "launch_ms": launch_stats(p_ms),
+            "frac_of_achievable": round(p_tflops / ach["mfma_bf16_tflops"], 4),
+            "scores_bytes_avoided": scores_bytes_avoided(wp["B"], wp["Hq"], wp["Sq"], wp["Sk"]),
         },
+        "achievable": ach,
         "interleaved": {
             "note": "same steps with prefill and decode alternating: the prefill then starts with caches "
                     "flushed by the preceding decode",
@@ -394,7 +529,7 @@ def main():
         "wall_s_timed": round(wall, 4),
         "kernel_source_digest": source_digest(),
     }
-    line["other_configs"] = other_configs(dev)
+    line["other_configs"] = other_configs(dev, ach)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

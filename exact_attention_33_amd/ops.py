@@ -22,9 +22,10 @@ STATUS_NAMES = {
     4: "ATTN_ERR_HEADDIM", 5: "ATTN_ERR_SPLITS", 6: "ATTN_ERR_WINDOW",
     7: "ATTN_ERR_WORKSPACE", 8: "ATTN_ERR_HIP", 9: "ATTN_ERR_ARG",
 }
-# every symbol include/attn.h declares
+# every symbol include/attn.h and include/attn_calib.h declare
 EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_bwd", "attn_decode", "attn_decode_ex",
-           "attn_decode_workspace_bytes", "attn_error_string", "attn_version")
+           "attn_decode_workspace_bytes", "attn_error_string", "attn_version",
+           "attn_calib_stream", "attn_calib_mfma", "attn_calib_mfma_flops")
 
 _lib = None
 
@@ -61,6 +62,12 @@ def lib() -> ctypes.CDLL:
     L.attn_error_string.restype = ctypes.c_char_p
     L.attn_version.argtypes = []
     L.attn_version.restype = ctypes.c_char_p
+    L.attn_calib_stream.argtypes = [vp, sz, vp, sz, vp]
+    L.attn_calib_stream.restype = i
+    L.attn_calib_mfma.argtypes = [vp, i, i, vp]
+    L.attn_calib_mfma.restype = i
+    L.attn_calib_mfma_flops.argtypes = [i, i]
+    L.attn_calib_mfma_flops.restype = ctypes.c_double
     _lib = L
     return L
 
@@ -216,3 +223,25 @@ def attn_decode_ex(q, kcache, vcache, num_splits, scale=None, out=None, lse=None
                                 Sk, D, int(num_splits), scale, _ptr(workspace), workspace.numel(),
                                 _stream(q)))
     return o, lse
+
+
+# ---- measurement reference kernels (include/attn_calib.h) -------------------
+
+def calib_stream(src: torch.Tensor, dst: torch.Tensor):
+    """dst chunk j (16 bytes) = XOR of src chunks j, j+n, j+2n, ... (n = dst chunks):
+    a plain HBM stream of src.nbytes read and dst.nbytes written."""
+    for t, n in ((src, "src"), (dst, "dst")):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous GPU tensor")
+    _check(lib().attn_calib_stream(_ptr(src), src.numel() * src.element_size(), _ptr(dst),
+                                   dst.numel() * dst.element_size(), _stream(dst)))
+    return dst
+
+
+def calib_mfma(out: torch.Tensor, workgroups: int, iters: int) -> float:
+    """A loop of bf16 MFMA instructions with no memory traffic; returns its flop count."""
+    _want(out, "out", torch.float32, 1, out.device)
+    if out.numel() < 4 * workgroups:
+        raise ValueError("out needs 4 floats per workgroup")
+    _check(lib().attn_calib_mfma(_ptr(out), int(workgroups), int(iters), _stream(out)))
+    return float(lib().attn_calib_mfma_flops(int(workgroups), int(iters)))
