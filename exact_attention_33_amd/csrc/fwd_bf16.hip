@@ -9,8 +9,11 @@
 // ybx.com, "FA3 innovations"), here with gfx950 means.
 //
 // Work decomposition
-//   * one workgroup = 4 wavefronts = BM = 128 query rows of one (b, h);
-//     each wavefront owns 32 rows.  Two workgroups share a CU.
+//   * one workgroup = NW wavefronts = BM = 32*NW query rows of one (b, h);
+//     each wavefront owns 32 rows.  D = 128: NW = 4, two workgroups share a
+//     CU.  D = 64: NW = 8 (256 rows), which halves the K/V tiles loaded per
+//     query row where a window or the causal mask limits the keys, and two
+//     such workgroups share a CU (four wavefronts per SIMD).
 //   * K and V tiles of BN keys stream HBM -> LDS by buffer loads that write
 //     LDS directly (no register staging); out-of-range keys read as zero.
 //     Two slots each: tile t+1 is in flight while tile t is multiplied.
@@ -64,8 +67,6 @@ struct FwdArgs {
   int xcd_heads;  // > 0: heads per XCD for the XCD-aware block order
 };
 
-constexpr int kBM = 128;
-constexpr int kThreads = 256;
 constexpr float kSlack = 8.0f;
 
 // LDS row of key `r` of a K tile: bits 2 and 3 swapped (an involution).
@@ -85,8 +86,9 @@ __device__ __forceinline__ int swz_v(int row) {
   else return ((row & 3) << 1) ^ ((row >> 2) & 7);
 }
 
-template <int D, int BN>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
+template <int D, int BN, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
+  constexpr int BM = 32 * NW;                     // query rows per workgroup
   constexpr int KCH = D / 8;                      // 16-byte chunks per row
   constexpr int NKB = BN / 32;                    // 32-key blocks per tile
   constexpr int NDB = D / 32;                     // 32-dim blocks of the output
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int VS = PAD ? D * 2 + 64 : D * 2;
   constexpr int KSLOT = BN * KS, VSLOT = BN * VS;
   constexpr int NB = (KSLOT + VSLOT) / 1024;     // 1 KB DMA blocks per (K, V) tile pair
-  constexpr int NBW = (NB + 3) / 4;              // per wavefront (at most)
+  constexpr int NBW = (NB + NW - 1) / NW;        // per wavefront (at most)
   static_assert(KSLOT % 1024 == 0 && VSLOT % 1024 == 0, "whole blocks");
   __shared__ __attribute__((aligned(1024))) char sK[2 * KSLOT];
   __shared__ __attribute__((aligned(1024))) char sV[2 * VSLOT];
@@ -127,8 +129,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int off = a.Sk - a.Sq;
   const int w = a.window;
 
-  const int r0 = qtile * kBM;
-  const int r1 = min(r0 + kBM, a.Sq) - 1;
+  const int r0 = qtile * BM;
+  const int r1 = min(r0 + BM, a.Sq) - 1;
   int kv_lo = 0, kv_hi = a.Sk;
   if (a.causal) kv_hi = min(kv_hi, r1 + off + 1);
   if (w >= 0) {
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   bool disk[NBW];
 #pragma unroll
   for (int i = 0; i < NBW; ++i) {
-    const int bb = i * 4 + wave;
+    const int bb = i * NW + wave;
     disk[i] = bb < KSLOT / 1024;
     if (disk[i]) {
       const int p = bb * 64 + lane;
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
       ddst[i] = (uint32_t)(vb * 1024);
     }
   }
-  const int nbw = (NB - wave + 3) / 4;   // blocks this wavefront issues
+  const int nbw = (NB - wave + NW - 1) / NW;   // blocks this wavefront issues
   const uint32_t sK0 = lds_addr(sK), sV0 = lds_addr(sV);
   auto issue = [&](int tile) {
     const int kt = tile * BN;
@@ -203,7 +205,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     const uint32_t kdst = sK0 + (tile & 1) * KSLOT, vdst = sV0 + (tile & 1) * VSLOT;
 #pragma unroll
     for (int i = 0; i < NBW - 1; ++i) dma16(disk[i] ? rk : rv, doff[i], (disk[i] ? kdst : vdst) + ddst[i]);
-    if (NB % 4 == 0 || nbw == NBW)
+    if (NB % NW == 0 || nbw == NBW)
       dma16(disk[NBW - 1] ? rk : rv, doff[NBW - 1], (disk[NBW - 1] ? kdst : vdst) + ddst[NBW - 1]);
   };
 
@@ -399,15 +401,16 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
   a.causal = s.causal;
   a.window = s.window;
   a.c2 = s.scale * kLog2e;
-  a.n_qtiles = (s.Sq + kBM - 1) / kBM;
+  const int bm = (s.D == 128) ? 128 : 256;
+  a.n_qtiles = (s.Sq + bm - 1) / bm;
   const int BH = s.B * s.Hq;
   const int64_t nblocks = (int64_t)a.n_qtiles * BH;
   a.xcd_heads = (BH % 8 == 0) ? BH / 8 : 0;
-  dim3 grid((unsigned)nblocks), block(kThreads);
+  dim3 grid((unsigned)nblocks), block(bm / 32 * 64);
   if (s.D == 128)
-    hipLaunchKernelGGL((fwd_bf16_kernel<128, 64>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, 4>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<64, 64>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, 8>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
