@@ -9,11 +9,11 @@
 // ybx.com, "FA3 innovations"), here with gfx950 means.
 //
 // Work decomposition
-//   * one workgroup = NW wavefronts = BM = 32*NW query rows of one (b, h);
-//     each wavefront owns 32 rows.  D = 128: NW = 4, two workgroups share a
-//     CU.  D = 64: NW = 8 (256 rows), which halves the K/V tiles loaded per
-//     query row where a window or the causal mask limits the keys, and two
-//     such workgroups share a CU (four wavefronts per SIMD).
+//   * one workgroup = NW = 8 wavefronts = BM = 256 query rows of one (b, h);
+//     each wavefront owns 32 rows.  Every K/V tile written to LDS is read by
+//     eight wavefronts, which halves the LDS write traffic and the K/V loads
+//     per query row compared with 128-row workgroups.  D = 128: one workgroup
+//     per CU (two wavefronts per SIMD); D = 64: two (four per SIMD).
 //   * K and V tiles of BN keys stream HBM -> LDS by buffer loads that write
 //     LDS directly (no register staging); out-of-range keys read as zero.
 //     Two slots each: tile t+1 is in flight while tile t is multiplied.
@@ -29,9 +29,9 @@
 //     [key][dim] tile.  P lines up with V because K rows sit in LDS with bits
 //     2 and 3 of the key index swapped inside each 32-key block, which makes
 //     the 8 keys a lane holds for each 16-key step consecutive.
-//   * two workgroups share each CU (one wavefront of each per SIMD) and are
-//     not coupled by barriers, so one wavefront's softmax overlaps the other's
-//     matrix-core work.  Apart from the rare wave-uniform rescale, the only
+//   * two or more wavefronts share each SIMD, so one wavefront's softmax
+//     overlaps another's matrix-core work.  Apart from the rare wave-uniform
+//     rescale, the only
 //     branch in the tile loop skips the matrix work of a tile no row of the
 //     wavefront can see (past the causal diagonal, outside the window); the
 //     accumulators keep one register home across it.
@@ -401,14 +401,14 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
   a.causal = s.causal;
   a.window = s.window;
   a.c2 = s.scale * kLog2e;
-  const int bm = (s.D == 128) ? 128 : 256;
+  const int bm = 256;   // 8 wavefronts of 32 rows
   a.n_qtiles = (s.Sq + bm - 1) / bm;
   const int BH = s.B * s.Hq;
   const int64_t nblocks = (int64_t)a.n_qtiles * BH;
   a.xcd_heads = (BH % 8 == 0) ? BH / 8 : 0;
   dim3 grid((unsigned)nblocks), block(bm / 32 * 64);
   if (s.D == 128)
-    hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, 4>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, 8>), grid, block, 0, stream, a);
   else
     hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, 8>), grid, block, 0, stream, a);
   return hipGetLastError();
