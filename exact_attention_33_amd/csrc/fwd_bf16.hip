@@ -14,10 +14,12 @@
 //     eight wavefronts, which halves the LDS write traffic and the K/V loads
 //     per query row compared with 128-row workgroups.  D = 128: one workgroup
 //     per CU (two wavefronts per SIMD); D = 64: two (four per SIMD).
-//   * K and V tiles of BN keys stream HBM -> LDS by buffer loads that write
-//     LDS directly (no register staging); out-of-range keys read as zero.
-//     Two slots each: tile t+1 is in flight while tile t is multiplied.
-//     One barrier per tile.
+//   * K and V tiles of BN keys (128 at D = 128, 64 at D = 64) stream HBM ->
+//     LDS by buffer loads that write LDS directly (no register staging);
+//     out-of-range keys read as zero.  Two slots each: tile t+1 is in flight
+//     while tile t is multiplied.  One barrier per tile.  (Three slots were
+//     measured slower; 128-key tiles at D = 64 need registers that cost a
+//     workgroup per CU.)
 //   * scores are computed transposed, S^T = K Q^T, on
 //     v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims from LDS, B = the Q
 //     fragment held in registers).  A lane then holds ONE query and 16 of a
@@ -408,7 +410,7 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
   a.xcd_heads = (BH % 8 == 0) ? BH / 8 : 0;
   dim3 grid((unsigned)nblocks), block(bm / 32 * 64);
   if (s.D == 128)
-    hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, 8>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, 128, 8>), grid, block, 0, stream, a);
   else
     hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, 8>), grid, block, 0, stream, a);
   return hipGetLastError();
