@@ -57,6 +57,32 @@ def draw_grad(shape, dtype: str, seed: int, device="cpu"):
     return torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(TORCH_DTYPES[dtype])
 
 
+E4M3_MAX = 448.0
+
+
+def quantize_e4m3(x: torch.Tensor):
+    """Per-tensor fp8 (OCP E4M3) codes of ``x`` for synthetic fp8 inputs: ``x`` is
+    divided by ``descale = amax / 448`` (so its largest magnitude maps to the
+    largest finite code), clamped to +-448 and rounded by torch's
+    float8_e4m3fn conversion.  Returns ``(codes as uint8, descale)``; the real
+    input is ``decode(code) * descale``."""
+    amax = float(x.abs().max())
+    descale = amax / E4M3_MAX if amax > 0 else 1.0
+    y = (x.float() / descale).clamp(-E4M3_MAX, E4M3_MAX)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8), descale
+
+
+def draw_qkv_fp8(q_shape, kv_shape, seed: int, device="cpu"):
+    """q, k, v drawn as in ``draw_qkv`` (fp32 N(0, 1), one generator) and each
+    quantized to e4m3 with its own per-tensor descale: returns
+    ``(q8, k8, v8, q_descale, k_descale, v_descale)``."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    out = [quantize_e4m3(torch.randn(sh, generator=gen, device=device, dtype=torch.float32))
+           for sh in (q_shape, kv_shape, kv_shape)]
+    return out[0][0], out[1][0], out[2][0], out[0][1], out[1][1], out[2][1]
+
+
 def workload_inputs(name: str, device="cpu", seed: int | None = None):
     """Inputs of a named workload: dict with q, k, v and the call parameters."""
     w = dict(WORKLOADS[name])

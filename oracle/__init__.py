@@ -34,6 +34,12 @@ What it computes, and where the pages state it:
   no backward algorithm).  Pinned by tests/pins_backward.py (central finite
   differences of ``attention``, torch autograd, closed-form special cases).
 
+* ``e4m3_decode`` / ``attention_fp8`` (``fp8.py``) -- the exact attention of
+  fp8 (OCP E4M3) inputs with per-tensor descale factors: the inputs decoded
+  to their real values, then ``attention``.  Pinned by tests/pins_fp8.py (all
+  256 codes against torch's float8_e4m3fn conversion and the format's closed
+  forms, descale identities).
+
 Every function is fp64 throughout.  Parity pins: see tests/test_oracle_pins.py
 (brute force, online == two-pass, split+tree == unsplit, uniform scores,
 permutation invariance, special cases, overflow safety, GQA == MHA, the
@@ -54,3 +60,4 @@ from .attention import (  # noqa: F401
     n_visible,
 )
 from .backward import attention_backward  # noqa: F401
+from .fp8 import E4M3_MAX, attention_fp8, e4m3_decode  # noqa: F401
