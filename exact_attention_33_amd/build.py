@@ -20,7 +20,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libattn.so")
-SOURCES = ["api.hip", "fwd_bf16.hip", "fwd_f32.hip", "decode.hip", "bwd.hip", "calib.hip"]
+SOURCES = ["api.hip", "fwd_bf16.hip", "fwd_fp8.hip", "fwd_f32.hip", "decode.hip", "bwd.hip", "calib.hip"]
 ARCH = "gfx950"
 
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -160,6 +160,22 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
                                       stream));
 }
 
+int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o, float* lse, int B, int Hq,
+                 int Hkv, int Sq, int Sk, int D, int causal, int window, float scale,
+                 float q_descale, float k_descale, float v_descale, hipStream_t stream) {
+  int st = check_fwd(q8, k8, v8, o, B, Hq, Hkv, Sq, Sk, D, causal, window, scale);
+  if (st != ATTN_OK) return st;
+  if (D != 128) return ATTN_ERR_HEADDIM;
+  if (check_scale(q_descale) != ATTN_OK || check_scale(k_descale) != ATTN_OK ||
+      check_scale(v_descale) != ATTN_OK)
+    return ATTN_ERR_ARG;
+  if ((int64_t)B * Hq * Sq == 0) return ATTN_OK;
+  return to_status(ea::launch_fwd_fp8((const uint8_t*)q8, (const uint8_t*)k8, (const uint8_t*)v8,
+                                      (uint16_t*)o, lse,
+                                      fwd_shape(B, Hq, Hkv, Sq, Sk, D, causal, window, scale),
+                                      q_descale, k_descale, v_descale, stream));
+}
+
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq, int Hkv,
              int Sq, int Sk, int D, int causal, int window, float scale, hipStream_t stream) {

@@ -23,7 +23,7 @@ STATUS_NAMES = {
     7: "ATTN_ERR_WORKSPACE", 8: "ATTN_ERR_HIP", 9: "ATTN_ERR_ARG",
 }
 # every symbol include/attn.h and include/attn_calib.h declare
-EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_bwd", "attn_decode", "attn_decode_ex",
+EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_fp8", "attn_bwd", "attn_decode", "attn_decode_ex",
            "attn_decode_workspace_bytes", "attn_error_string", "attn_version",
            "attn_calib_stream", "attn_calib_mfma", "attn_calib_mfma_flops")
 
@@ -50,6 +50,8 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd.restype = i
     L.attn_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
     L.attn_fwd_f32.restype = i
+    L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, f, f, f, vp]
+    L.attn_fwd_fp8.restype = i
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
     L.attn_bwd.restype = i
     L.attn_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp]
@@ -139,6 +141,41 @@ def attn_fwd(q, k, v, causal=False, window=-1, scale=None, out=None, lse=None, r
 def attn_fwd_f32(q, k, v, causal=False, window=-1, scale=None, out=None, lse=None, return_lse=True):
     """Prefill on fp32 tensors (no bf16 rounding anywhere) -> ``(o, lse)``."""
     return _fwd(lib().attn_fwd_f32, torch.float32, q, k, v, causal, window, scale, out, lse, return_lse)
+
+
+def attn_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal=False, window=-1, scale=None,
+                 out=None, lse=None, return_lse=True):
+    """Prefill on fp8 (OCP E4M3) codes: ``q8 [B,Hq,Sq,D]``, ``k8, v8 [B,Hkv,Sk,D]`` as
+    uint8 tensors (or torch.float8_e4m3fn), one descale per tensor -> ``(o bf16, lse)``."""
+    dev = q8.device
+    if dev.type != "cuda":
+        raise ValueError("q8 must be on a GPU")
+    codes = []
+    for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        if isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn:
+            t = t.view(torch.uint8)
+        _want(t, n, torch.uint8, 4, dev)
+        codes.append(t)
+    q8, k8, v8 = codes
+    B, Hq, Sq, D = q8.shape
+    Bk, Hkv, Sk, Dk = k8.shape
+    if v8.shape != k8.shape or Bk != B or Dk != D:
+        raise ValueError(f"shape mismatch q{tuple(q8.shape)} k{tuple(k8.shape)} v{tuple(v8.shape)}")
+    o = torch.empty((B, Hq, Sq, D), dtype=torch.bfloat16, device=dev) if out is None else out
+    _want(o, "out", torch.bfloat16, 4, dev)
+    if tuple(o.shape) != (B, Hq, Sq, D):
+        raise ValueError("out must have q's shape")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _want(lse, "lse", torch.float32, 3, dev)
+        if tuple(lse.shape) != (B, Hq, Sq):
+            raise ValueError("lse must be [B, Hq, Sq]")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib().attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Sk, D,
+                              int(causal), int(window), scale, float(q_descale), float(k_descale),
+                              float(v_descale), _stream(q8)))
+    return o, lse
 
 
 def attn_bwd(q, k, v, o, dout, lse, causal=False, window=-1, scale=None, dq=None, dk=None, dv=None,

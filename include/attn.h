@@ -83,6 +83,30 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
                  int causal, int window, float scale, hipStream_t stream);
 
 /*
+ * Prefill on fp8 inputs: q, k, v are OCP FP8 E4M3 ("e4m3fn") byte codes with
+ * one descale factor per tensor; the result is the attention of the real
+ * inputs decode(code) * descale, with o in bf16 and lse in fp32 (natural log,
+ * scale and descales included).  FlashAttention-3 takes attention to
+ * low-precision FP8 (FlashAttention explainer, aiunderstanding.org, "The
+ * future of FlashAttention" and the FAQ entry on FlashAttention-3;
+ * FlashAttention-3 article, ybx.com, "FA3 innovations" point 3); the pages fix
+ * no format or scaling, these are readings.
+ *
+ *   q8      : uint8 codes [B, Hq, Sq, D].   k8, v8: uint8 codes [B, Hkv, Sk, D].
+ *   o       : bf16 [B, Hq, Sq, D].           lse: fp32 [B, Hq, Sq] or NULL.
+ *   D       : 128 only (ATTN_ERR_HEADDIM otherwise).
+ *   q_descale, k_descale, v_descale: finite and > 0 (ATTN_ERR_ARG otherwise).
+ *   Other arguments and errors as attn_fwd.
+ * The probabilities are rounded to e4m3 (round to nearest even) before the
+ * p.v product on the fp8 matrix cores; scores, softmax and accumulation are
+ * fp32; o is rounded once to bf16.
+ */
+int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o, float* lse,
+                 int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                 int causal, int window, float scale,
+                 float q_descale, float k_descale, float v_descale, hipStream_t stream);
+
+/*
  * Backward of attn_fwd (bf16): the gradients of sum(dout * o) with respect to
  * q, k and v, with o = softmax(scale * q k^T) v under the same causal /
  * window / GQA rules.  The pages name training as a use of the fused method

@@ -134,3 +134,18 @@ def test_calib_validation(L):
     assert L.attn_calib_mfma(FAKE, -1, 10, None) == ARG
     assert L.attn_calib_mfma(FAKE, 4, -1, None) == ARG
     assert L.attn_calib_mfma_flops(3, 5) == 2.0 * 32 * 32 * 16 * 4 * 4 * 5 * 3
+
+
+def test_fwd_fp8_validation(L):
+    f = ctypes.c_float
+
+    def call(D=128, qd=1.0, kd=1.0, vd=1.0, q=FAKE, Sq=8):
+        return L.attn_fwd_fp8(q, FAKE, FAKE, FAKE, None, 1, 2, 1, Sq, 8, D, 0, -1, f(0.125),
+                              f(qd), f(kd), f(vd), None)
+
+    assert call(D=64) == HEADDIM
+    assert call(qd=0.0) == ARG
+    assert call(kd=-1.0) == ARG
+    assert call(vd=float("inf")) == ARG
+    assert call(q=None) == NULL
+    assert call(q=None, Sq=0) == OK          # nothing to compute
