@@ -35,10 +35,11 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, published
 
 PREFILL = "causal_prefill"
 DECODE = "gqa_decode"
-KERNEL_SOURCES = ["fwd_bf16.hip", "decode.hip", "bwd.hip", "common.h"]
+KERNEL_SOURCES = ["fwd_bf16.hip", "fwd_fp8.hip", "decode.hip", "bwd.hip", "common.h"]
 
 
 def visible_pairs_causal(Sq: int, Sk: int) -> int:
@@ -328,7 +329,25 @@ def other_configs(dev, ach, iters: int = 50):
         "note": "dq kernel + dk/dv kernel; algorithmic work counts S, dP, dV, dK, dQ once (the kernels "
                 "recompute S and dP in both passes)",
     }
-    del wp, do, op, lp, dq, dk, dv, delta
+    # the causal prefill on fp8 (e4m3) inputs, one descale per tensor
+    q8, k8, v8, qd, kd, vd = synth.draw_qkv_fp8(wp["q"].shape, wp["k"].shape, wp["seed"], dev)
+    o8 = torch.empty_like(wp["q"])
+
+    def run_f(i):
+        ops.attn_fwd_fp8(q8, k8, v8, qd, kd, vd, causal=True, scale=wp["scale"], out=o8, lse=lp)
+
+    st = launch_stats(time_launches(run_f, iters, stream))
+    ms = st["avg_ms"]
+    fl = prefill_flops(wp)
+    tf = fl / (ms * 1e-3) / 1e12
+    out["fp8_causal_prefill"] = {
+        "shape": {k: wp[k] for k in ("B", "Hq", "Hkv", "Sq", "D")}, "avg_launch_ms": ms, "launch_ms": st,
+        "bound": "mfma", "tflops": round(tf, 1), "peak": PEAK_FP8_TFLOPS,
+        "frac_of_mfma_peak": round(tf / PEAK_FP8_TFLOPS, 4), "algorithmic_flops": fl,
+        "traffic": measured_traffic("fp8_prefill"),
+        "note": "q, k, v as e4m3 codes with per-tensor descales; p rounded to e4m3 for the p.v product",
+    }
+    del wp, do, op, lp, dq, dk, dv, delta, q8, k8, v8, o8
     torch.cuda.empty_cache()
     return out
 
@@ -341,7 +360,15 @@ def run_only(name: str, steps: int, warmup: int, dev):
     from exact_attention_33_amd import ops, synth
 
     stream = torch.cuda.current_stream(dev)
-    if name in ("causal_prefill", "window_encoder", "global_layer", "backward"):
+    if name == "fp8_prefill":
+        w = synth.workload_inputs("causal_prefill", dev)
+        q8, k8, v8, qd, kd, vd = synth.draw_qkv_fp8(w["q"].shape, w["k"].shape, w["seed"], dev)
+        o = torch.empty_like(w["q"])
+        lse = torch.empty(w["B"], w["Hq"], w["Sq"], dtype=torch.float32, device=dev)
+
+        def fn(i):
+            ops.attn_fwd_fp8(q8, k8, v8, qd, kd, vd, causal=True, scale=w["scale"], out=o, lse=lse)
+    elif name in ("causal_prefill", "window_encoder", "global_layer", "backward"):
         w = synth.workload_inputs("window_encoder" if name == "global_layer" else
                                   ("causal_prefill" if name == "backward" else name), dev)
         window = -1 if name == "global_layer" else w["window"]
@@ -393,7 +420,8 @@ def main():
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--only", default=None,
                     help="time one workload alone and print its launch statistics (for profilers): "
-                         "causal_prefill, window_encoder, global_layer, backward, gqa_decode, long_decode")
+                         "causal_prefill, fp8_prefill, window_encoder, global_layer, backward, gqa_decode, "
+                         "long_decode")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
