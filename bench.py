@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, published
+WARM_MS = 50.0               # minimum untimed busy time before a timed series
 
 PREFILL = "causal_prefill"
 DECODE = "gqa_decode"
@@ -69,12 +70,26 @@ def launch_stats(ms):
             "p10_ms": round(pct(0.1), 5), "p90_ms": round(pct(0.9), 5)}
 
 
-def time_launches(fn, iters: int, stream, warm: int = 10):
-    """Per-launch durations (ms) of fn(i), HIP events recorded on `stream`."""
+def time_launches(fn, iters: int, stream, warm: int = 10, warm_ms: float = WARM_MS):
+    """Per-launch durations (ms) of fn(i), HIP events recorded on `stream`.
+
+    Untimed warm-up: `warm` launches, then more until `warm_ms` of wall time
+    has passed with the GPU busy, so the timed launches run at the clock a
+    sustained load settles at (after short warm-ups the same kernel measured
+    up to 18 % slower)."""
+    import time
+
     import torch
 
     for i in range(warm):
         fn(i)
+    torch.cuda.synchronize()
+    t0, n = time.perf_counter(), 0
+    while (time.perf_counter() - t0) * 1e3 < warm_ms:
+        for _ in range(8):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(iters)]
     for i in range(iters):
         ev[i][0].record(stream)
