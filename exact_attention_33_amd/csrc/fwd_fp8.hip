@@ -51,7 +51,7 @@ struct Fp8Args {
 constexpr int kNW8 = 8;                 // wavefronts per workgroup
 constexpr int kBM8 = 32 * kNW8;         // query rows per workgroup
 constexpr int kBN8 = 128;               // keys per tile
-constexpr float kSlack8 = 8.0f;
+constexpr float kSlackP8 = 256.0f;      // largest probability before a rescale
 
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
   // formats 0/0 = E4M3 for both operands; block scales 127 = 2^0
@@ -231,36 +231,49 @@ __global__ __launch_bounds__(64 * kNW8, 2) void fwd_fp8_kernel(Fp8Args a) {
           st[bk][r] = ((c >= lo) & (c <= hi)) ? st[bk][r] : kNegInf;
         }
     }
-    float mx = kNegInf;
-#pragma unroll
-    for (int bk = 0; bk < 2; ++bk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[bk][r]);
-    mx = max_swap32(mx) * c2;
-    if (__any(mx > m_run + kSlack8)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+    // Probabilities against the running max as it stands: while no p
+    // exceeds 2^8 (the rescale slack) the row max need not be known.  A row
+    // that has seen no key yet, or a sum above 2^8, takes the exact path:
+    // row max, rescale of O and l when it rose by more than the slack,
+    // probabilities again.
     float rs = 0.f;
     i32x8 pf;   // byte j = probability of key kg0 + 32*hh + j, e4m3
+    auto probs = [&](float m_use) {
+      rs = 0.f;
 #pragma unroll
-    for (int bk = 0; bk < 2; ++bk)
+      for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
-      for (int r = 0; r < 16; r += 4) {
-        const float p0 = fast_exp2(__builtin_fmaf(st[bk][r + 0], c2, -m_use));
-        const float p1 = fast_exp2(__builtin_fmaf(st[bk][r + 1], c2, -m_use));
-        const float p2 = fast_exp2(__builtin_fmaf(st[bk][r + 2], c2, -m_use));
-        const float p3 = fast_exp2(__builtin_fmaf(st[bk][r + 3], c2, -m_use));
-        rs += (p0 + p1) + (p2 + p3);
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
-        pf[(16 * bk + r) >> 2] = word;
+        for (int r = 0; r < 16; r += 4) {
+          const float p0 = fast_exp2(__builtin_fmaf(st[bk][r + 0], c2, -m_use));
+          const float p1 = fast_exp2(__builtin_fmaf(st[bk][r + 1], c2, -m_use));
+          const float p2 = fast_exp2(__builtin_fmaf(st[bk][r + 2], c2, -m_use));
+          const float p3 = fast_exp2(__builtin_fmaf(st[bk][r + 3], c2, -m_use));
+          rs += (p0 + p1) + (p2 + p3);
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+          word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
+          pf[(16 * bk + r) >> 2] = word;
+        }
+    };
+    probs(m_run);
+    if (__any((m_run == kNegInf) | (rs > kSlackP8))) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[bk][r]);
+      mx = max_swap32(mx) * c2;
+      // move to the exact max (not only past the slack), so that rows of
+      // many moderate scores do not come back to this path
+      if (__any(mx > m_run)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+        m_run = m_new;
       }
+      probs((m_run == kNegInf) ? 0.f : m_run);
+    }
     l_run += rs;
     // O^T += V^T P^T over the group's 64 keys
 #pragma unroll
