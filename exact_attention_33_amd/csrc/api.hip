@@ -165,7 +165,6 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o, float*
                  float q_descale, float k_descale, float v_descale, hipStream_t stream) {
   int st = check_fwd(q8, k8, v8, o, B, Hq, Hkv, Sq, Sk, D, causal, window, scale);
   if (st != ATTN_OK) return st;
-  if (D != 128) return ATTN_ERR_HEADDIM;
   if (check_scale(q_descale) != ATTN_OK || check_scale(k_descale) != ATTN_OK ||
       check_scale(v_descale) != ATTN_OK)
     return ATTN_ERR_ARG;

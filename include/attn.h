@@ -94,7 +94,7 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
  *
  *   q8      : uint8 codes [B, Hq, Sq, D].   k8, v8: uint8 codes [B, Hkv, Sk, D].
  *   o       : bf16 [B, Hq, Sq, D].           lse: fp32 [B, Hq, Sq] or NULL.
- *   D       : 128 only (ATTN_ERR_HEADDIM otherwise).
+ *   D       : 64 or 128 (ATTN_ERR_HEADDIM otherwise), as attn_fwd.
  *   q_descale, k_descale, v_descale: finite and > 0 (ATTN_ERR_ARG otherwise).
  *   Other arguments and errors as attn_fwd.
  * The probabilities are rounded to e4m3 (round to nearest even) before the

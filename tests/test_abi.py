@@ -143,7 +143,7 @@ def test_fwd_fp8_validation(L):
         return L.attn_fwd_fp8(q, FAKE, FAKE, FAKE, None, 1, 2, 1, Sq, 8, D, 0, -1, f(0.125),
                               f(qd), f(kd), f(vd), None)
 
-    assert call(D=64) == HEADDIM
+    assert call(D=96) == HEADDIM
     assert call(qd=0.0) == ARG
     assert call(kd=-1.0) == ARG
     assert call(vd=float("inf")) == ARG

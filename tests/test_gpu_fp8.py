@@ -72,8 +72,9 @@ def _check(o, lse, host, desc, scale, causal, window, rows=None):
 
 
 def _rows_ref(host, desc, scale, causal, window, rows):
-    """Oracle on the sampled query rows only: the key range a row sees does not
-    depend on the other rows, so rows are computed one by one."""
+    """Oracle on the sampled query rows only: the keys a row sees do not
+    depend on the other rows, so each row is the unmasked attention over its
+    own visible key range [lo, hi] (bottom-right causal alignment)."""
     q8, k8, v8 = host
     qd, kd, vd = desc
     B, Hq, Sq, D = q8.shape
@@ -81,18 +82,20 @@ def _rows_ref(host, desc, scale, causal, window, rows):
     o = np.zeros((B, Hq, len(rows), D))
     lse = np.zeros((B, Hq, len(rows)))
     G = Hq // k8.shape[1]
-    assert window < 0, "row sampling is written for masks without a window"
     for b in range(B):
         for h in range(Hq):
             g = h // G
             for n, r in enumerate(rows):
-                # one row on its own: with Sq = 1 the row sits at the last
-                # key position, so keep the keys up to the row's own position
-                keep = r + (Sk - Sq) + 1 if causal else Sk
+                pos = r + (Sk - Sq)
+                lo, hi = 0, Sk - 1
+                if causal:
+                    hi = min(hi, pos)
+                if window >= 0:
+                    lo, hi = max(lo, pos - window), min(hi, pos + window)
                 qq = q8[b:b + 1, h:h + 1, r:r + 1]
-                kk, vv = k8[b:b + 1, g:g + 1], v8[b:b + 1, g:g + 1]
-                oo, ll = oracle.attention_fp8(qq, kk[:, :, :keep], vv[:, :, :keep], qd, kd, vd, scale,
-                                              bool(causal), window)
+                kk = k8[b:b + 1, g:g + 1, lo:hi + 1]
+                vv = v8[b:b + 1, g:g + 1, lo:hi + 1]
+                oo, ll = oracle.attention_fp8(qq, kk, vv, qd, kd, vd, scale, False, -1)
                 o[b, h, n] = oo[0, 0, 0]
                 lse[b, h, n] = ll[0, 0, 0]
     return o, lse
@@ -113,6 +116,18 @@ def test_fp8_parity(shape):
     _check(o, lse, host, desc, scale, causal, window)
 
 
+@pytest.mark.parametrize("shape", [
+    (1, 2, 2, 300, 300, 1, -1),      # causal, ragged tail
+    (1, 4, 2, 513, 513, 0, -1),      # GQA 2:1, ragged
+    (1, 2, 2, 700, 700, 0, 64),      # the encoder's window, several tiles
+    (2, 2, 1, 200, 600, 1, 40),      # Sq != Sk, causal + window
+], ids=lambda s: "B{}Hq{}Hkv{}Sq{}Sk{}c{}w{}".format(*s))
+def test_fp8_parity_d64(shape):
+    B, Hq, Hkv, Sq, Sk, causal, window = shape
+    o, lse, host, desc, scale = _case(B, Hq, Hkv, Sq, Sk, causal, window, seed=sum(shape) + 64, D=64)
+    _check(o, lse, host, desc, scale, causal, window)
+
+
 def test_fp8_peaky():
     """scale = 1: rows dominated by a few keys, where the e4m3 rounding of p
     shows undiluted."""
@@ -128,14 +143,23 @@ def test_fp8_causal_prefill_full_size_sampled_rows():
     _check(o, lse, host, desc, scale, 1, -1, rows=rows)
 
 
+def test_fp8_window_encoder_full_size_sampled_rows():
+    """The window-encoder shape (B8 H12 S8192 D64, |i-j| <= 64) on fp8 inputs,
+    in the launch configuration the benchmark times, on sampled rows (both
+    ends, tile edges, the window's reach)."""
+    o, lse, host, desc, scale = _case(8, 12, 12, 8192, 8192, 0, 64, seed=2, D=64)
+    rows = [0, 1, 63, 64, 65, 255, 256, 4095, 8127, 8191]
+    _check(o, lse, host, desc, scale, 0, 64, rows=rows)
+
+
 def test_fp8_empty_and_errors():
     q8 = torch.zeros((1, 2, 0, 128), dtype=torch.uint8, device=DEV)
     k8 = torch.zeros((1, 2, 16, 128), dtype=torch.uint8, device=DEV)
     o, lse = ops.attn_fwd_fp8(q8, k8, k8, 1.0, 1.0, 1.0)
     assert o.shape == (1, 2, 0, 128)
-    q64 = torch.zeros((1, 2, 8, 64), dtype=torch.uint8, device=DEV)
+    q96 = torch.zeros((1, 2, 8, 96), dtype=torch.uint8, device=DEV)
     with pytest.raises(ops.AttnError) as e:
-        ops.attn_fwd_fp8(q64, q64, q64, 1.0, 1.0, 1.0)
+        ops.attn_fwd_fp8(q96, q96, q96, 1.0, 1.0, 1.0)
     assert e.value.status == 4   # ATTN_ERR_HEADDIM
     q8 = torch.zeros((1, 2, 8, 128), dtype=torch.uint8, device=DEV)
     with pytest.raises(ops.AttnError) as e:
