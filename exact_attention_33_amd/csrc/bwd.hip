@@ -297,14 +297,19 @@ __global__ __launch_bounds__(kThreadsB, 2) void bwd_dkdv_kernel(BwdArgs a) {
   }
   if (!k_ok) row_hi = -1;
 
-  uint32_t doff[NBW], ddst[NBW];
+  // Source offsets of this lane's DMA chunks, two 16-bit offsets per
+  // register (a tile is at most 8 KB; 0xffff lies past every tile's buffer
+  // range and reads zero): at 256 VGPRs a register more spills, and a
+  // spilled offset's reload waits for the stage's own DMA loads.
+  uint32_t doffp[(NBW + 1) / 2] = {}, ddst[NBW];
   bool disq[NBW];
 #pragma unroll
   for (int i = 0; i < NBW; ++i) {
     const int bb = i * 4 + wave;
     disq[i] = bb < G::BLK;
     const int tb = disq[i] ? bb : bb - G::BLK;
-    doff[i] = tile_src<D>(tb * 64 + lane);
+    const uint32_t o = tile_src<D>(tb * 64 + lane);
+    doffp[i >> 1] |= (o < 0xffffu ? o : 0xffffu) << (16 * (i & 1));
     ddst[i] = (uint32_t)(bb * 1024);
   }
   const uint32_t sT0 = lds_addr(&sT[0][0]);
@@ -319,7 +324,13 @@ __global__ __launch_bounds__(kThreadsB, 2) void bwd_dkdv_kernel(BwdArgs a) {
     const uint32_t base = sT0 + st * STAGE;
 #pragma unroll
     for (int i = 0; i < NBW; ++i)
-      if (i * 4 + wave < NB2) dma16(disq[i] ? rq : rd, doff[i], base + ddst[i]);
+      if (i * 4 + wave < NB2) {
+        // unpacked here, at the load (volatile keeps the compiler from
+        // hoisting five unpacked registers out of the loop)
+        uint32_t o;
+        asm volatile("v_bfe_u32 %0, %1, %2, 16" : "=v"(o) : "v"(doffp[i >> 1]), "i"(16 * (i & 1)));
+        dma16(disq[i] ? rq : rd, o, base + ddst[i]);
+      }
     if (wave == 0) {
       const uint32_t lo = (lane < 8) ? (uint32_t)(lane * 16) : 0x7ffffff0u;
       dma16(make_rsrc(a.lse + qb + qt, rows * 4), lo, base + 2 * G::BYTES);
