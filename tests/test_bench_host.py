@@ -1,0 +1,84 @@
+"""Host-side arithmetic of bench.py (CPU only): the algorithmic work and bytes
+each roofline divides by, checked against counts derived here from the mask
+definitions by brute force or closed form, and the one-GPU guard."""
+
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from exact_attention_33_amd import synth  # noqa: E402
+
+
+def _pairs_brute(Sq, Sk, causal, window):
+    """Visible (query, key) pairs counted one by one (bottom-right causal)."""
+    off = Sk - Sq
+    n = 0
+    for i in range(Sq):
+        c = i + off
+        for j in range(Sk):
+            ok = True
+            if causal:
+                ok = ok and j <= c
+            if window >= 0:
+                ok = ok and abs(c - j) <= window
+            n += ok
+    return n
+
+
+@pytest.mark.parametrize("Sq,Sk", [(1, 1), (5, 5), (7, 19), (19, 7), (64, 64), (33, 100)])
+def test_visible_pairs_causal_brute(Sq, Sk):
+    assert bench.visible_pairs_causal(Sq, Sk) == _pairs_brute(Sq, Sk, True, -1)
+
+
+def test_causal_prefill_work():
+    # S (S + 1) / 2 pairs per head: 2,098,176 at S = 2048, times 64 heads
+    w = dict(synth.WORKLOADS["causal_prefill"])
+    assert bench.visible_pairs_causal(2048, 2048) == 2048 * 2049 // 2 == 2_098_176
+    assert bench.prefill_flops(w) == 4 * 128 * 2_098_176 * 64
+    assert abs(bench.prefill_flops(w) / 1e9 - 68.75) < 0.01
+
+
+def test_window_encoder_work_and_bytes():
+    w = dict(synth.WORKLOADS["window_encoder"])
+    S, wd = w["Sq"], w["window"]
+    # interior rows see 2w + 1 keys; the first and last w rows lose 1 .. w
+    pairs = S * (2 * wd + 1) - wd * (wd + 1)
+    assert pairs == _pairs_brute(300, 300, False, 64) + (S - 300) * (2 * wd + 1)
+    assert bench.window_flops(w) == 4.0 * w["D"] * pairs * w["B"] * w["Hq"]
+    assert abs(bench.window_flops(w) / 1e9 - 25.87) < 0.01
+    n = w["B"] * w["Hq"] * S * w["D"]
+    assert bench.window_bytes(w) == 2 * 4 * n + 4 * w["B"] * w["Hq"] * S
+    assert abs(bench.window_bytes(w) / 1e6 - 405.8) < 0.1
+
+
+def test_decode_kv_bytes():
+    w4 = dict(synth.WORKLOADS["gqa_decode"])
+    w5 = dict(synth.WORKLOADS["long_decode"])
+    assert bench.decode_kv_bytes(w4) == 2 * 16 * 8 * 32768 * 128 * 2 == 2 ** 31
+    assert bench.decode_kv_bytes(w5) == 2 * 1 * 8 * 2 ** 20 * 128 * 2 == 2 ** 32
+
+
+def test_launch_stats():
+    st = bench.launch_stats([0.5, 0.1, 0.4, 0.2, 0.3])
+    assert st["n"] == 5 and st["avg_ms"] == 0.3 and st["median_ms"] == 0.3
+    assert st["p10_ms"] == 0.1 and st["p90_ms"] == 0.5
+
+
+def test_scores_bytes_avoided():
+    # S and P, each written once and read once, in bf16
+    assert bench.scores_bytes_avoided(4, 16, 2048, 2048) == 4 * 2 * 4 * 16 * 2048 * 2048
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
