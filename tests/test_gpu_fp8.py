@@ -109,6 +109,7 @@ def _rows_ref(host, desc, scale, causal, window, rows):
     (1, 2, 2, 500, 500, 1, 40),      # causal + window
     (1, 1, 1, 33, 97, 0, -1),        # tiny, Sq != Sk
     (1, 2, 2, 1024, 1024, 1, -1),    # several full tiles
+    (1, 2, 1, 600, 200, 1, -1),      # Sq > Sk causal: the first 400 rows see no key
 ], ids=lambda s: "B{}Hq{}Hkv{}Sq{}Sk{}c{}w{}".format(*s))
 def test_fp8_parity(shape):
     B, Hq, Hkv, Sq, Sk, causal, window = shape
@@ -121,6 +122,7 @@ def test_fp8_parity(shape):
     (1, 4, 2, 513, 513, 0, -1),      # GQA 2:1, ragged
     (1, 2, 2, 700, 700, 0, 64),      # the encoder's window, several tiles
     (2, 2, 1, 200, 600, 1, 40),      # Sq != Sk, causal + window
+    (1, 2, 2, 300, 100, 1, 16),      # Sq > Sk, causal + window: rows without keys
 ], ids=lambda s: "B{}Hq{}Hkv{}Sq{}Sk{}c{}w{}".format(*s))
 def test_fp8_parity_d64(shape):
     B, Hq, Hkv, Sq, Sk, causal, window = shape
