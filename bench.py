@@ -464,7 +464,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=60,
+    ap.add_argument("--warmup", type=int, default=200,
                     help="untimed steps first; the GPU needs tens of milliseconds of work to reach its steady clock")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
