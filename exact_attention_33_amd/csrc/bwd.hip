@@ -91,7 +91,11 @@ __global__ __launch_bounds__(kThreadsB, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char sT[2][4 * G::BYTES];
 
   const int BH = a.B * a.Hq;
-  const int bh = blockIdx.x % BH, qtile = blockIdx.x / BH;
+  // causal: the heaviest query tiles (most keys) first, so they do not
+  // start last and set the kernel's tail
+  const int nq = (a.Sq + 127) / 128;
+  const int bh = blockIdx.x % BH, rank = blockIdx.x / BH;
+  const int qtile = a.causal ? nq - 1 - rank : rank;
   const int b = bh / a.Hq, h = bh % a.Hq;
   const int g = h / (a.Hq / a.Hkv);
   const int tid = threadIdx.x, lane = tid & 63;
