@@ -11,13 +11,16 @@
 //   dv = P^T dout,  dk = scale dS^T q,  dq = scale dS k.
 //
 // Two kernels, launched in this order on one stream:
-//   * bwd_dq_kernel: one workgroup = 4 wavefronts x 32 query rows of one
-//     (b, h).  q and dout stay in registers; K/V tiles of 64 keys (two
-//     32-key halves per barrier) stream through LDS.  Per tile and wavefront: S^T = K q^T and dP^T = V dout^T
-//     (A = 32 keys from LDS, B = the wavefront's 32 queries in registers),
-//     so a lane holds one query and its lse / delta are lane scalars; then
-//     dq^T += K^T dS^T with K^T read by the transposing LDS load.  It first
-//     computes delta for its rows and writes it for the second kernel.
+//   * bwd_dq_kernel: one workgroup = 8 wavefronts x 32 query rows of one
+//     (b, h), causal tiles heaviest first.  q and dout stay in registers;
+//     K/V tiles of 64 keys (two 32-key halves per barrier) stream through
+//     LDS, each shared by the 8 wavefronts.  Per tile and wavefront: S^T = K
+//     q^T and dP^T = V dout^T (A = 32 keys from LDS, B = the wavefront's 32
+//     queries in registers), so a lane holds one query and its lse / delta
+//     are lane scalars; then dq^T += K^T dS^T with K^T read by the
+//     transposing LDS load.  A 32-key half no row of the wavefront sees is
+//     skipped.  It first computes delta for its rows and writes it for the
+//     second kernel.
 //   * bwd_dkdv_kernel: one workgroup = 4 wavefronts x 32 keys of one
 //     (b, kv head).  k and v stay in registers; q / dout tiles of 32 rows of
 //     every query head of the GQA group stream through LDS (with their lse
@@ -25,8 +28,9 @@
 //     from LDS, B = the wavefront's keys), a lane holding one key; then
 //     dv^T += dout^T P and dk^T += q^T dS.  The group's query heads are summed
 //     in registers, so no atomics are needed.
-// Both kernels run two wavefronts per SIMD (two workgroups per CU), so one
-// wavefront's softmax-side vector work overlaps the other's matrix work.
+// Both kernels run two wavefronts per SIMD (one dq workgroup or two dk/dv
+// workgroups per CU), so one wavefront's softmax-side vector work overlaps
+// the other's matrix work.
 // The A-operand rows of S / S^T and dP / dP^T are read with bits 2 and 3 of
 // the row index swapped; the 8 values a lane then holds for each 16-row
 // MFMA step are consecutive rows, which is the B-operand layout of the
@@ -37,7 +41,9 @@
 namespace ea {
 namespace {
 
-constexpr int kThreadsB = 256;
+constexpr int kThreadsB = 256;      // dk/dv kernel: 4 wavefronts x 32 keys
+constexpr int kThreadsDq = 512;     // dq kernel: 8 wavefronts x 32 query rows
+constexpr int kRowsDq = kThreadsDq / 2;
 constexpr float kBwdLog2e = 1.4426950408889634f;
 
 struct BwdArgs {
@@ -82,18 +88,18 @@ __device__ __forceinline__ uint32_t tile_src(int p) {
 
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreadsB, 2) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreadsDq, 2) void bwd_dq_kernel(BwdArgs a) {
   using G = TileGeo<D>;
   constexpr int NQK = D / 16;    // k-steps over dims
   constexpr int NDB = D / 32;    // 32-dim blocks of dq^T
   // a stage holds 64 keys as four padded 32-row tiles: K0 | K1 | V0 | V1;
-  // wavefront w loads tile w
+  // wavefronts 2t and 2t+1 load tile t, half of its 1 KB blocks each
   __shared__ __attribute__((aligned(1024))) char sT[2][4 * G::BYTES];
 
   const int BH = a.B * a.Hq;
   // causal: the heaviest query tiles (most keys) first, so they do not
   // start last and set the kernel's tail
-  const int nq = (a.Sq + 127) / 128;
+  const int nq = (a.Sq + kRowsDq - 1) / kRowsDq;
   const int bh = blockIdx.x % BH, rank = blockIdx.x / BH;
   const int qtile = a.causal ? nq - 1 - rank : rank;
   const int b = bh / a.Hq, h = bh % a.Hq;
@@ -104,8 +110,8 @@ __global__ __launch_bounds__(kThreadsB, 2) void bwd_dq_kernel(BwdArgs a) {
   const int off = a.Sk - a.Sq;
   const int w = a.window;
 
-  const int r0 = qtile * 128;
-  const int r1 = min(r0 + 128, a.Sq) - 1;
+  const int r0 = qtile * kRowsDq;
+  const int r1 = min(r0 + kRowsDq, a.Sq) - 1;
   int kv_lo = 0, kv_hi = a.Sk;
   if (a.causal) kv_hi = min(kv_hi, r1 + off + 1);
   if (w >= 0) {
@@ -124,6 +130,7 @@ __global__ __launch_bounds__(kThreadsB, 2) void bwd_dq_kernel(BwdArgs a) {
   const int qi = qw0 + l32;
   const bool q_ok = qi < a.Sq;
   const int pos = qi + off;
+  const int plo = qw0 + off, phi = min(qw0 + 31, a.Sq - 1) + off;   // this wavefront's positions
 
   // q and dout of this lane's row (B operands), delta from o and dout
   bf16x8 qf[NQK], df[NQK];
@@ -157,20 +164,25 @@ __global__ __launch_bounds__(kThreadsB, 2) void bwd_dq_kernel(BwdArgs a) {
   }
   if (!q_ok) key_hi = -1;
 
-  // tile loads: wavefront w fills tile w of the stage (K0, K1, V0, V1)
-  uint32_t doff[G::BLK];
+  // tile loads: wavefronts 2t and 2t+1 fill tile t of the stage (K0, K1,
+  // V0, V1), blocks [0, HB) and [HB, BLK) of it
+  constexpr int HB = (G::BLK + 1) / 2;
+  const int tw = wave >> 1, half = wave & 1;
+  const int nblk = half ? G::BLK - HB : HB;
+  uint32_t doff[HB];
 #pragma unroll
-  for (int i = 0; i < G::BLK; ++i) doff[i] = tile_src<D>(i * 64 + lane);
-  const uint16_t* src_base = (wave < 2) ? kh : vh;
-  const int src_half = (wave & 1) * 32;
+  for (int i = 0; i < HB; ++i) doff[i] = tile_src<D>((half * HB + i) * 64 + lane);
+  const uint16_t* src_base = (tw < 2) ? kh : vh;
+  const int src_half = (tw & 1) * 32;
   const uint32_t sT0 = lds_addr(&sT[0][0]);
   auto issue = [&](int tile, int st) {
     const int kt = tile * 64 + src_half;
     const int rows = max(0, min(32, a.Sk - kt));
     const auto rs = make_rsrc(src_base + (size_t)(rows > 0 ? kt : 0) * D, (uint32_t)(rows * D * 2));
-    const uint32_t base = sT0 + st * (4 * G::BYTES) + wave * G::BYTES;
+    const uint32_t base = sT0 + st * (4 * G::BYTES) + tw * G::BYTES + half * HB * 1024;
 #pragma unroll
-    for (int i = 0; i < G::BLK; ++i) dma16(rs, doff[i], base + i * 1024);
+    for (int i = 0; i < HB; ++i)
+      if (i < nblk) dma16(rs, doff[i], base + i * 1024);
   };
 
   // lane bases of the operand reads inside one tile
@@ -192,6 +204,12 @@ __global__ __launch_bounds__(kThreadsB, 2) void bwd_dq_kernel(BwdArgs a) {
     if (tile + 1 < t_end) issue(tile + 1, st ^ 1);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
+    // skip a 32-key block no row of this wavefront can see
+    const int kb0 = tile * 64 + 32 * j;
+    bool any = kb0 < a.Sk;
+    if (a.causal) any = any && (kb0 <= phi);
+    if (w >= 0) any = any && (kb0 <= phi + w) && (kb0 + 31 >= plo - w);
+    if (!any) continue;
     const char* kb = &sT[st][j * G::BYTES];
     const char* vb = &sT[st][(2 + j) * G::BYTES];
 
@@ -459,13 +477,13 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
   a.window = s.window;
   a.c2 = s.scale * kBwdLog2e;
   a.scale = s.scale;
-  const int64_t nq = (int64_t)((s.Sq + 127) / 128) * s.B * s.Hq;
+  const int64_t nq = (int64_t)((s.Sq + kRowsDq - 1) / kRowsDq) * s.B * s.Hq;
   const int64_t nk = (int64_t)((s.Sk + 127) / 128) * s.B * s.Hkv;
   if (s.D == 128) {
-    if (nq > 0) hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)nq), dim3(kThreadsB), 0, stream, a);
+    if (nq > 0) hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)nq), dim3(kThreadsDq), 0, stream, a);
     if (nk > 0) hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)nk), dim3(kThreadsB), 0, stream, a);
   } else {
-    if (nq > 0) hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)nq), dim3(kThreadsB), 0, stream, a);
+    if (nq > 0) hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)nq), dim3(kThreadsDq), 0, stream, a);
     if (nk > 0) hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)nk), dim3(kThreadsB), 0, stream, a);
   }
   return hipGetLastError();
