@@ -13,12 +13,13 @@
 // Two kernels, launched in this order on one stream:
 //   * bwd_dq_kernel: one workgroup = 8 wavefronts x 32 query rows of one
 //     (b, h), causal tiles heaviest first.  q and dout stay in registers;
-//     K/V tiles of 64 keys (two 32-key halves per barrier) stream through
-//     LDS, each shared by the 8 wavefronts.  Per tile and wavefront: S^T = K
+//     K/V stages of 128 keys (four 32-key blocks per barrier, each of the 8
+//     wavefronts loading one K or V tile) stream through LDS, shared by the
+//     8 wavefronts.  Per tile and wavefront: S^T = K
 //     q^T and dP^T = V dout^T (A = 32 keys from LDS, B = the wavefront's 32
 //     queries in registers), so a lane holds one query and its lse / delta
 //     are lane scalars; then dq^T += K^T dS^T with K^T read by the
-//     transposing LDS load.  A 32-key half no row of the wavefront sees is
+//     transposing LDS load.  A 32-key block no row of the wavefront sees is
 //     skipped.  It first computes delta for its rows and writes it for the
 //     second kernel.
 //   * bwd_dkdv_kernel: one workgroup = 4 wavefronts x 32 keys of one
@@ -92,9 +93,10 @@ __global__ __launch_bounds__(kThreadsDq, 2) void bwd_dq_kernel(BwdArgs a) {
   using G = TileGeo<D>;
   constexpr int NQK = D / 16;    // k-steps over dims
   constexpr int NDB = D / 32;    // 32-dim blocks of dq^T
-  // a stage holds 64 keys as four padded 32-row tiles: K0 | K1 | V0 | V1;
-  // wavefronts 2t and 2t+1 load tile t, half of its 1 KB blocks each
-  __shared__ __attribute__((aligned(1024))) char sT[2][4 * G::BYTES];
+  // a stage holds 128 keys as eight padded 32-row tiles: K0..K3 | V0..V3;
+  // wavefront w loads tile w
+  constexpr int NJ = 4;                       // 32-key blocks per stage
+  __shared__ __attribute__((aligned(1024))) char sT[2][2 * NJ * G::BYTES];
 
   const int BH = a.B * a.Hq;
   // causal: the heaviest query tiles (most keys) first, so they do not
@@ -118,8 +120,8 @@ __global__ __launch_bounds__(kThreadsDq, 2) void bwd_dq_kernel(BwdArgs a) {
     kv_lo = max(kv_lo, r0 + off - w);
     kv_hi = min(kv_hi, r1 + off + w + 1);
   }
-  const int t_begin = max(kv_lo, 0) / 64;
-  const int t_end = (kv_hi > kv_lo) ? (kv_hi + 63) / 64 : t_begin;
+  const int t_begin = max(kv_lo, 0) / (32 * NJ);
+  const int t_end = (kv_hi > kv_lo) ? (kv_hi + 32 * NJ - 1) / (32 * NJ) : t_begin;
 
   const size_t q_base = ((size_t)b * a.Hq + h) * (size_t)a.Sq;
   const size_t kv_base = ((size_t)b * a.Hkv + g) * (size_t)a.Sk;
@@ -164,25 +166,20 @@ __global__ __launch_bounds__(kThreadsDq, 2) void bwd_dq_kernel(BwdArgs a) {
   }
   if (!q_ok) key_hi = -1;
 
-  // tile loads: wavefronts 2t and 2t+1 fill tile t of the stage (K0, K1,
-  // V0, V1), blocks [0, HB) and [HB, BLK) of it
-  constexpr int HB = (G::BLK + 1) / 2;
-  const int tw = wave >> 1, half = wave & 1;
-  const int nblk = half ? G::BLK - HB : HB;
-  uint32_t doff[HB];
+  // tile loads: wavefront w fills tile w of the stage (K0..K3, V0..V3)
+  uint32_t doff[G::BLK];
 #pragma unroll
-  for (int i = 0; i < HB; ++i) doff[i] = tile_src<D>((half * HB + i) * 64 + lane);
-  const uint16_t* src_base = (tw < 2) ? kh : vh;
-  const int src_half = (tw & 1) * 32;
+  for (int i = 0; i < G::BLK; ++i) doff[i] = tile_src<D>(i * 64 + lane);
+  const uint16_t* src_base = (wave < NJ) ? kh : vh;
+  const int src_off = (wave % NJ) * 32;
   const uint32_t sT0 = lds_addr(&sT[0][0]);
   auto issue = [&](int tile, int st) {
-    const int kt = tile * 64 + src_half;
+    const int kt = tile * 32 * NJ + src_off;
     const int rows = max(0, min(32, a.Sk - kt));
     const auto rs = make_rsrc(src_base + (size_t)(rows > 0 ? kt : 0) * D, (uint32_t)(rows * D * 2));
-    const uint32_t base = sT0 + st * (4 * G::BYTES) + tw * G::BYTES + half * HB * 1024;
+    const uint32_t base = sT0 + st * (2 * NJ * G::BYTES) + wave * G::BYTES;
 #pragma unroll
-    for (int i = 0; i < HB; ++i)
-      if (i < nblk) dma16(rs, doff[i], base + i * 1024);
+    for (int i = 0; i < G::BLK; ++i) dma16(rs, doff[i], base + i * 1024);
   };
 
   // lane bases of the operand reads inside one tile
@@ -203,15 +200,15 @@ __global__ __launch_bounds__(kThreadsDq, 2) void bwd_dq_kernel(BwdArgs a) {
     __syncthreads();
     if (tile + 1 < t_end) issue(tile + 1, st ^ 1);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NJ; ++j) {
     // skip a 32-key block no row of this wavefront can see
-    const int kb0 = tile * 64 + 32 * j;
+    const int kb0 = tile * 32 * NJ + 32 * j;
     bool any = kb0 < a.Sk;
     if (a.causal) any = any && (kb0 <= phi);
     if (w >= 0) any = any && (kb0 <= phi + w) && (kb0 + 31 >= plo - w);
     if (!any) continue;
     const char* kb = &sT[st][j * G::BYTES];
-    const char* vb = &sT[st][(2 + j) * G::BYTES];
+    const char* vb = &sT[st][(NJ + j) * G::BYTES];
 
     // S^T = K q^T, dP^T = V dout^T (32 keys x 32 queries each)
     f32x16 s = f32x16{}, dp = f32x16{};
@@ -223,7 +220,7 @@ __global__ __launch_bounds__(kThreadsDq, 2) void bwd_dq_kernel(BwdArgs a) {
       dp = mfma32(va, df[t], dp);
     }
     // element r holds key kt0 + 16*(r/8) + 8*hh + r%8 of this lane's query
-    const int kt0 = tile * 64 + 32 * j;
+    const int kt0 = tile * 32 * NJ + 32 * j;
     const int lo = key_lo - kt0 - 8 * hh, hi = key_hi - kt0 - 8 * hh;
     bf16x8 dsb[2];
 #pragma unroll
