@@ -369,6 +369,23 @@ def other_configs(dev, ach, iters: int = 50):
         "note": "dq kernel + dk/dv kernel; algorithmic work counts S, dP, dV, dK, dQ once (the kernels "
                 "recompute S and dP in both passes)",
     }
+    # one long sequence through the same prefill kernel (B1 H16 S8192 D128),
+    # where the per-workgroup start and end weigh less than at S = 2048
+    ql, kl, vl = synth.draw_qkv((1, 16, 8192, 128), (1, 16, 8192, 128), "bf16", 9, dev)
+    ol = torch.empty_like(ql)
+    ll = torch.empty(1, 16, 8192, dtype=torch.float32, device=dev)
+    for causal in (1, 0):
+        stl = launch_stats(time_launches(
+            lambda i: ops.attn_fwd(ql, kl, vl, causal=bool(causal), scale=wp["scale"], out=ol, lse=ll), 20, stream))
+        wl_ = dict(B=1, Hq=16, Sq=8192, Sk=8192, D=128)
+        fl = prefill_flops(wl_) if causal else 4.0 * 128 * 8192 * 8192 * 16
+        tf = fl / (stl["avg_ms"] * 1e-3) / 1e12
+        out["long_prefill_causal" if causal else "long_prefill"] = {
+            "shape": {**wl_, "causal": causal}, "avg_launch_ms": stl["avg_ms"], "launch_ms": stl,
+            "bound": "mfma", "tflops": round(tf, 1), "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "frac_of_achievable": round(tf / ach["mfma_bf16_tflops"], 4), "algorithmic_flops": fl,
+        }
+    del ql, kl, vl, ol, ll
     # the causal prefill on fp8 (e4m3) inputs, one descale per tensor
     q8, k8, v8, qd, kd, vd = synth.draw_qkv_fp8(wp["q"].shape, wp["k"].shape, wp["seed"], dev)
     o8 = torch.empty_like(wp["q"])

@@ -270,6 +270,24 @@ def test_runs_on_the_callers_stream():
 # Encoder stack pattern: the global layer of the window-encoder shape
 # --------------------------------------------------------------------------
 
+@pytest.mark.parametrize("causal", [1, 0])
+def test_long_prefill_sampled_rows(causal):
+    """One long sequence, B1 H16 S8192 D128 (the benchmark's long-prefill
+    line), checked on sampled rows including tile edges and both ends."""
+    B, H, S, D = 1, 16, 8192, 128
+    q, k, v = synth.draw_qkv((B, H, S, D), (B, H, S, D), "bf16", 9, DEV)
+    scale = synth.default_scale(D)
+    announce(f"long prefill B1 H16 S8192 D128 causal{causal}, sampled rows")
+    o, lse = ops.attn_fwd(q, k, v, causal=bool(causal), scale=scale)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 255, 256, 4095, 4096, 8190, 8191])
+    o_ref, lse_ref = oracle.attention(to_numpy_exact(q), to_numpy_exact(k), to_numpy_exact(v), scale,
+                                      bool(causal), -1, rows=rows)
+    e = check_o(o[:, :, rows], o_ref, "bf16", "long prefill")
+    le = check_lse(lse[:, :, rows], lse_ref, "bf16", "long prefill")
+    announce(f"long prefill: {e} lse_err {le:.3g}")
+
+
 def test_encoder_global_layer_sampled_rows():
     """Full attention (no mask) at the window-encoder shape B8 H12 S8192 D64,
     the global layer that the local/global encoder pattern interleaves with
