@@ -244,18 +244,9 @@ __global__ __launch_bounds__(kThreadsDq, 2) void bwd_dq_kernel(BwdArgs a) {
     }
   }
 
-  if (q_ok) {
-    uint16_t* orow = a.dq + (q_base + qi) * D;
+  uint16_t* orow = a.dq + (q_base + (q_ok ? qi : 0)) * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        bf16x4 ov;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(acc[db][4 * g4 + j] * a.scale);
-        *(bf16x4*)(orow + db * 32 + 8 * g4 + 4 * hh) = ov;
-      }
-  }
+  for (int db = 0; db < NDB; ++db) store_row32_bf16(orow + db * 32, acc[db], a.scale, hh, q_ok);
 }
 
 // ---------------------------------------------------------------------------
@@ -430,6 +421,8 @@ __global__ __launch_bounds__(kThreadsB, 2) void bwd_dkdv_kernel(BwdArgs a) {
       }
   }
 
+  // 8-byte stores here: at 256 VGPRs the exchange of the 16-byte store
+  // helper costs a register, which spills inside the loop
   if (k_ok) {
     uint16_t* krow = a.dk + (kv_base + kk) * D;
     uint16_t* vrow = a.dv + (kv_base + kk) * D;

@@ -90,6 +90,44 @@ __device__ __forceinline__ float sum_swap32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Write one 32-column block of a row held in the layout of a 32x32 MFMA
+// result whose columns are the rows of the output: lane l has element
+// 4g + j (g, j = 0..3) of column 8g + 4*(l/32) + j.  The values are scaled,
+// rounded to bf16 and, after one exchange between lanes l and l+32 per pair
+// of 4-column chunks (v_permlane32_swap moves lanes 32..63 of its first
+// operand and lanes 0..31 of its second), each lane writes 8 consecutive
+// columns with one 16-byte store: half the store instructions of 8-byte
+// stores, and 32 contiguous bytes per row per instruction.  Every lane must
+// call this (the exchange is cross-lane); `ok` gates only the store.
+__device__ __forceinline__ void store_row32_bf16(uint16_t* dst, const f32x16& acc, float mul, int hh, bool ok) {
+  uint32_t pk[4][2];
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4) {
+    bf16x4 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = (__bf16)(acc[4 * g4 + j] * mul);
+    const u32x2 u = __builtin_bit_cast(u32x2, v);
+    pk[g4][0] = u[0];
+    pk[g4][1] = u[1];
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    // lower lanes keep chunk 2p and receive the partner's chunk 2p; upper
+    // lanes keep chunk 2p+1 and receive the partner's chunk 2p+1
+    uint32_t x[2], y[2];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const auto r = __builtin_amdgcn_permlane32_swap(pk[2 * p][w], pk[2 * p + 1][w], false, false);
+      x[w] = r[0];
+      y[w] = r[1];
+    }
+    if (ok) {
+      const u32x4 v4 = {x[0], x[1], y[0], y[1]};
+      *(u32x4*)(dst + 8 * (2 * p + hh)) = v4;
+    }
+  }
+}
+
 // Two bf16 (low halves / high halves of two packed words) into one word:
 // result.lo = x.half, result.hi = y.half.
 __device__ __forceinline__ uint32_t pack_lo(uint32_t x, uint32_t y) {

@@ -310,20 +310,11 @@ __global__ __launch_bounds__(64 * kNW8, 2) void fwd_fp8_kernel(Fp8Args a) {
   // ---- epilogue: o = v_descale * acc / l in bf16, lse in natural log -------
   const float l_tot = sum_swap32(l_run);
   const float inv = (l_tot > 0.f) ? a.v_descale / l_tot : 0.f;
-  if (q_ok) {
-    uint16_t* orow = a.o + (q_base + qi) * D;
+  uint16_t* orow = a.o + (q_base + (q_ok ? qi : 0)) * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        bf16x4 ov;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(oacc[db][4 * g4 + e] * inv);
-        *(bf16x4*)(orow + db * 32 + 8 * g4 + 4 * hh) = ov;
-      }
-    if (a.lse != nullptr && hh == 0)
-      a.lse[q_base + qi] = (l_tot > 0.f) ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
-  }
+  for (int db = 0; db < NDB; ++db) store_row32_bf16(orow + db * 32, oacc[db], inv, hh, q_ok);
+  if (q_ok && a.lse != nullptr && hh == 0)
+    a.lse[q_base + qi] = (l_tot > 0.f) ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
 }
 
 }  // namespace
