@@ -48,8 +48,6 @@ struct Fp8Args {
   int xcd_heads;
 };
 
-constexpr int kNW8 = 8;                 // wavefronts per workgroup
-constexpr int kBM8 = 32 * kNW8;         // query rows per workgroup
 constexpr float kSlackP8 = 256.0f;      // largest probability before a rescale
 
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
@@ -73,10 +71,10 @@ __device__ __forceinline__ int k8_row_key(int R) {
   return 64 * grp + 32 * hh + 16 * b + r;
 }
 
-template <int D, int BN>
-__global__ __launch_bounds__(64 * kNW8, 2) void fwd_fp8_kernel(Fp8Args a) {
+template <int D, int BN, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void fwd_fp8_kernel(Fp8Args a) {
   static_assert(D == 64 || D == 128, "head dims 64 and 128");
-  constexpr int NW = kNW8, BM = kBM8;
+  constexpr int BM = 32 * NW;          // query rows per workgroup
   static_assert(BN % 64 == 0, "whole 64-key groups");
   constexpr int NDB = D / 32;          // 32-dim blocks of O
   constexpr int NKT = D / 64;          // k-steps of S (64 dims each)
@@ -337,7 +335,10 @@ hipError_t launch_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, 
   a.window = s.window;
   a.c2 = s.scale * q_descale * k_descale * kLog2e;
   a.v_descale = v_descale;
-  a.n_qtiles = (s.Sq + kBM8 - 1) / kBM8;
+  // 8 wavefronts of 32 rows; 4 for a sliding window at D = 64 (see the bf16 launcher)
+  const bool narrow = (s.D == 64) && (s.window >= 0);
+  const int bm = narrow ? 128 : 256;
+  a.n_qtiles = (s.Sq + bm - 1) / bm;
   const int BH = s.B * s.Hq;
   const int64_t nblocks = (int64_t)a.n_qtiles * BH;
   a.xcd_heads = (BH % 8 == 0) ? BH / 8 : 0;
@@ -345,9 +346,12 @@ hipError_t launch_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, 
   // 384 rather than 512 keys for a +-64 window around 256 rows, but measured
   // slower (twice the barriers and DMA rounds per byte)
   if (s.D == 128)
-    hipLaunchKernelGGL((fwd_fp8_kernel<128, 128>), dim3((unsigned)nblocks), dim3(64 * kNW8), 0, stream, a);
+    hipLaunchKernelGGL((fwd_fp8_kernel<128, 128, 8>), dim3((unsigned)nblocks), dim3(512), 0, stream, a);
   else
-    hipLaunchKernelGGL((fwd_fp8_kernel<64, 128>), dim3((unsigned)nblocks), dim3(64 * kNW8), 0, stream, a);
+    if (narrow)
+      hipLaunchKernelGGL((fwd_fp8_kernel<64, 128, 4>), dim3((unsigned)nblocks), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((fwd_fp8_kernel<64, 128, 8>), dim3((unsigned)nblocks), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
