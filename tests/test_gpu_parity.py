@@ -174,6 +174,9 @@ DECODE_SHAPES = [
     (3, 32, 8, 4097, 128, 64),
     (1, 32, 1, 3000, 128, 16),            # 32 query heads per kv head: two head groups
     (1, 16, 16, 2048, 64, 1),
+    (2, 8, 2, 3000, 128, 65),             # 65 partials: one wavefront's 64 leaves plus one
+    (1, 8, 2, 5000, 64, 200),             # four combine wavefronts, the last with 8 leaves
+    (832, 1, 1, 8, 64, 2),                # many (b, h) rows, two keys each
     (1, 8, 2, 2000, 128, 300),            # > 256 partials: two combine levels
     (1, 4, 2, 70000, 64, 70000),          # one key per chunk, three combine levels
 ]
