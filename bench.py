@@ -494,7 +494,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
+              "(the library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
 
     import torch
