@@ -128,8 +128,9 @@ def _fwd(fn, dtype, q, k, v, causal, window, scale, out, lse, return_lse):
         if tuple(lse.shape) != (B, Hq, Sq):
             raise ValueError("lse must be [B, Hq, Sq]")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Sk, D,
-              int(causal), int(window), scale, _stream(q)))
+    with torch.cuda.device(q.device):  # kernels launch on the current device
+        _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Sk, D,
+                  int(causal), int(window), scale, _stream(q)))
     return o, lse
 
 
@@ -172,9 +173,10 @@ def attn_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal=False, wind
         if tuple(lse.shape) != (B, Hq, Sq):
             raise ValueError("lse must be [B, Hq, Sq]")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    _check(lib().attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Sk, D,
-                              int(causal), int(window), scale, float(q_descale), float(k_descale),
-                              float(v_descale), _stream(q8)))
+    with torch.cuda.device(q8.device):  # kernels launch on the current device
+        _check(lib().attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Sk, D,
+                                  int(causal), int(window), scale, float(q_descale), float(k_descale),
+                                  float(v_descale), _stream(q8)))
     return o, lse
 
 
@@ -209,9 +211,10 @@ def attn_bwd(q, k, v, o, dout, lse, causal=False, window=-1, scale=None, dq=None
     if tuple(delta.shape) != (B, Hq, Sq):
         raise ValueError("delta must be [B, Hq, Sq]")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    _check(lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
-                          _ptr(dv), _ptr(delta), B, Hq, Hkv, Sq, Sk, D, int(causal), int(window), scale,
-                          _stream(q)))
+    with torch.cuda.device(q.device):  # kernels launch on the current device
+        _check(lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                              _ptr(dv), _ptr(delta), B, Hq, Hkv, Sq, Sk, D, int(causal), int(window), scale,
+                              _stream(q)))
     return dq, dk, dv
 
 
@@ -236,8 +239,9 @@ def _decode_shapes(q, kcache, vcache, out):
 def attn_decode(q, kcache, vcache, num_splits, out=None):
     """Split-KV decode with the library workspace, scale 1/sqrt(D) -> ``o [B,Hq,D]``."""
     B, Hq, Hkv, Sk, D, o = _decode_shapes(q, kcache, vcache, out)
-    _check(lib().attn_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(o), B, Hq, Hkv, Sk, D,
-                             int(num_splits), _stream(q)))
+    with torch.cuda.device(q.device):  # kernels launch on the current device
+        _check(lib().attn_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(o), B, Hq, Hkv, Sk, D,
+                                 int(num_splits), _stream(q)))
     return o
 
 
@@ -252,13 +256,17 @@ def attn_decode_ex(q, kcache, vcache, num_splits, scale=None, out=None, lse=None
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     if lse is not None:
         _want(lse, "lse", torch.float32, 2, q.device)
+        if tuple(lse.shape) != (B, Hq):
+            raise ValueError("lse must be [B, Hq]")
     need = decode_workspace_bytes(B, Hq, D, int(num_splits)) if num_splits >= 1 else 0
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _want(workspace, "workspace", torch.uint8, 1, q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    _check(lib().attn_decode_ex(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(o), _ptr(lse), B, Hq, Hkv,
-                                Sk, D, int(num_splits), scale, _ptr(workspace), workspace.numel(),
-                                _stream(q)))
+    with torch.cuda.device(q.device):  # kernels launch on the current device
+        _check(lib().attn_decode_ex(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(o), _ptr(lse), B, Hq, Hkv,
+                                    Sk, D, int(num_splits), scale, _ptr(workspace), workspace.numel(),
+                                    _stream(q)))
     return o, lse
 
 

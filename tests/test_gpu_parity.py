@@ -208,6 +208,22 @@ def test_decode_peaky_and_planted():
     check_lse(lse, lse_ref, "bf16", "planted")
 
 
+def test_binding_rejects_bad_workspace_and_lse():
+    """The binding refuses, before any launch, a workspace of the wrong dtype
+    or in host memory and an lse of the wrong shape."""
+    announce("binding checks")
+    q, k, v = synth.draw_qkv((2, 4, 128), (2, 2, 100, 128), "bf16", 3, DEV)
+    with pytest.raises(ValueError):
+        ops.attn_decode_ex(q, k, v, 4, workspace=torch.zeros(1 << 20, dtype=torch.float32, device=DEV))
+    with pytest.raises(ValueError):
+        ops.attn_decode_ex(q, k, v, 4, workspace=torch.zeros(1 << 20, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        ops.attn_decode_ex(q, k, v, 4, lse=torch.empty(2, 5, device=DEV))
+    o, _ = ops.attn_decode_ex(q, k, v, 4, workspace=torch.zeros(1 << 20, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+
+
 def test_decode_empty_cache():
     announce("decode Sk = 0")
     q = torch.randn(2, 4, 128, device=DEV).to(torch.bfloat16)
