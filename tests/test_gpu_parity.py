@@ -285,6 +285,52 @@ def test_runs_on_the_callers_stream():
     assert torch.equal(o, ref)
 
 
+def test_graph_replay():
+    """The prefill, the fp8 prefill, the backward and the decode (caller
+    workspace) captured in one HIP graph: every replay, with eager work and
+    synchronisations between replays, gives the eager results bit for bit."""
+    announce("graph capture and replay")
+    q, k, v = synth.draw_qkv((2, 4, 333, 128), (2, 2, 333, 128), "bf16", 5, DEV)
+    q8, k8, v8, qd, kd, vd = synth.draw_qkv_fp8((1, 4, 200, 64), (1, 4, 200, 64), 6, DEV)
+    qd1, kd1, vd1 = synth.draw_qkv((4, 8, 128), (4, 2, 3000, 128), "bf16", 7, DEV)
+    do = synth.draw_grad(q.shape, "bf16", 8, DEV)
+    ns = 37
+    ws = torch.zeros(ops.decode_workspace_bytes(4, 8, 128, ns), dtype=torch.uint8, device=DEV)
+    bufs = dict(o=torch.empty_like(q), lse=torch.empty(2, 4, 333, device=DEV),
+                o8=torch.empty(1, 4, 200, 64, dtype=torch.bfloat16, device=DEV),
+                lse8=torch.empty(1, 4, 200, device=DEV),
+                od=torch.empty_like(qd1), lsed=torch.empty(4, 8, device=DEV),
+                dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+                delta=torch.empty(2, 4, 333, device=DEV))
+
+    def work():
+        ops.attn_fwd(q, k, v, causal=True, out=bufs["o"], lse=bufs["lse"])
+        ops.attn_fwd_fp8(q8, k8, v8, qd, kd, vd, window=17, out=bufs["o8"], lse=bufs["lse8"])
+        ops.attn_bwd(q, k, v, bufs["o"], do, bufs["lse"], causal=True, dq=bufs["dq"], dk=bufs["dk"],
+                     dv=bufs["dv"], delta=bufs["delta"])
+        ops.attn_decode_ex(qd1, kd1, vd1, ns, out=bufs["od"], lse=bufs["lsed"], workspace=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()  # eager, on the capture stream
+    torch.cuda.synchronize()
+    ref = {n: t.clone() for n, t in bufs.items()}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        work()
+    for rep in range(3):
+        for t in bufs.values():
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n, t in bufs.items():
+            assert torch.equal(t, ref[n]), (rep, n)
+        work()  # eager work between replays
+        torch.cuda.synchronize()
+
+
 # --------------------------------------------------------------------------
 # Encoder stack pattern: the global layer of the window-encoder shape
 # --------------------------------------------------------------------------
