@@ -224,6 +224,18 @@ def test_binding_rejects_bad_workspace_and_lse():
     assert torch.isfinite(o.float()).all()
 
 
+def test_decode_library_workspace_grows():
+    """attn_decode's own workspace grows on demand: a small call, a call that
+    needs more, then a small one again each give attn_decode_ex's bits."""
+    for i, (B, Hq, Hkv, Sk, ns) in enumerate([(1, 4, 1, 500, 3), (8, 32, 8, 4000, 200), (2, 8, 2, 900, 5)]):
+        q, k, v = synth.draw_qkv((B, Hq, 128), (B, Hkv, Sk, 128), "bf16", 40 + i, DEV)
+        announce(f"attn_decode library workspace B{B} Hq{Hq} Hkv{Hkv} Sk{Sk} ns{ns}")
+        o1 = ops.attn_decode(q, k, v, ns)
+        o2, _ = ops.attn_decode_ex(q, k, v, ns)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2)
+
+
 def test_decode_empty_cache():
     announce("decode Sk = 0")
     q = torch.randn(2, 4, 128, device=DEV).to(torch.bfloat16)
