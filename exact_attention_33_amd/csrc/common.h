@@ -55,13 +55,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // bytes land at LDS byte address lds_base + 16*i (lds_base wave-uniform).
 // Issued from asm so the compiler does not guard later LDS reads with a
 // blanket vmcnt(0); completion is awaited explicitly (vmcnt) by the caller.
-// The block sets M0 itself right before the load; the compiler treats M0 as
-// reserved and ignores the clobber, and no compiler-generated code in these
-// kernels reads M0 (checked in the emitted ISA), so nothing depends on its
-// value across blocks.
+// The LDS base goes in as an M0 operand ("{m0}"), so the compiler sets M0
+// itself before the block and knows its value.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(rs) : "memory", "m0");
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rs), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base)) : "memory");
 }
 
 // Wait until at most N vector-memory loads of this wave are outstanding.
