@@ -5,7 +5,8 @@
 // (express24.ir page), here on one device.
 //
 // Split kernel: one workgroup per (chunk, kv head, batch[, group of 16 query
-// heads]).  It streams its chunk of K and V from HBM exactly once and serves
+// heads]); when those groups divide evenly over the 8 XCDs, each XCD takes
+// whole groups, chunk after chunk.  It streams its chunk of K and V from HBM exactly once and serves
 // every query head that shares the kv head (GQA), which keeps the kernel at
 // one read of the cache -- the quantity that bounds decode.  Each of the 4
 // wavefronts takes every 4th 32-key step of the chunk:
@@ -44,6 +45,7 @@ struct SplitArgs {
   float* po;   // [B*Hq][ns][D] unnormalised accumulators
   float* pml;  // [B*Hq][ns][2] (m in base-2 units, l)
   int B, Hq, Hkv, Sk, ns, L, nhg;
+  int xcd_groups;  // B*Hkv*nhg % 8 == 0: XCD-aware block order
   float c2;  // scale * log2(e)
 };
 
@@ -55,13 +57,22 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
   __shared__ float sM[4][16];
   __shared__ float sL[4][16];
 
-  int bid = blockIdx.x;
-  const int c = bid % a.ns;
-  bid /= a.ns;
-  const int g = bid % a.Hkv;
-  bid /= a.Hkv;
-  const int hg = bid % a.nhg;
-  const int b = bid / a.nhg;
+  // (b, kv head, head group) = group.  Blocks are dispatched round-robin over
+  // the 8 XCDs; when the groups divide evenly, each XCD streams whole groups,
+  // chunk after chunk, so a group's KV goes through one XCD's L2.
+  int c, grp;
+  if (a.xcd_groups) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    c = slot % a.ns;
+    grp = (slot / a.ns) * 8 + xcd;
+  } else {
+    c = blockIdx.x % a.ns;
+    grp = blockIdx.x / a.ns;
+  }
+  const int g = grp % a.Hkv;
+  grp /= a.Hkv;
+  const int hg = grp % a.nhg;
+  const int b = grp / a.nhg;
   const int G = a.Hq / a.Hkv;
   const int h0 = g * G + hg * 16;
   const int nh = min(16, G - hg * 16);
@@ -352,6 +363,7 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v
   a.ns = s.num_splits;
   a.L = (int)(((int64_t)s.Sk + s.num_splits - 1) / s.num_splits);
   a.nhg = (G + 15) / 16;
+  a.xcd_groups = ((int64_t)s.B * s.Hkv * a.nhg) % 8 == 0;
   a.c2 = s.scale * kLog2e;
   dim3 grid((unsigned)((int64_t)s.num_splits * s.Hkv * s.B * a.nhg)), block(256);
   if (s.D == 128)
