@@ -174,55 +174,80 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(budget_s: float = 20.0):
-    """The fp64 oracle, untuned, on a bounded sample of the same workloads."""
-    import numpy as np
-    import torch
-
-    import oracle
-    from exact_attention_33_amd import synth
-
+def _blas_info():
     try:
         from threadpoolctl import threadpool_info
         blas = [(i.get("internal_api"), i.get("version"), i.get("num_threads")) for i in threadpool_info()]
         threads = max([n for _, _, n in blas if n] or [1])
     except Exception:  # noqa: BLE001
         blas, threads = [], 1
-    wp = synth.WORKLOADS[PREFILL]
-    wd = synth.WORKLOADS[DECODE]
-    scale_p = synth.default_scale(wp["D"])
-    # prefill sample: (b, h) heads of the causal workload, one at a time, until
-    # half the budget is spent or all 64 are done
-    nh, tp = 0, 0.0
-    while tp < budget_s / 2 and nh < wp["B"] * wp["Hq"]:
-        q, k, v = synth.draw_qkv((1, 1, wp["Sq"], wp["D"]), (1, 1, wp["Sk"], wp["D"]), "bf16", 100 + nh)
-        qn, kn, vn = (synth.to_numpy_exact(t) for t in (q, k, v))
-        t0 = time.perf_counter()
-        oracle.attention(qn, kn, vn, scale_p, True)
-        tp += time.perf_counter() - t0
-        nh += 1
-    flops = 4.0 * wp["D"] * visible_pairs_causal(wp["Sq"], wp["Sk"]) * nh
-    # decode sample: batch rows of the GQA decode workload, same rule
-    nb, td, kv_bytes = 0, 0.0, 0.0
-    while td < budget_s / 2 and nb < wd["B"]:
-        q, k, v = synth.draw_qkv((1, wd["Hq"], wd["D"]), (1, wd["Hkv"], wd["Sk"], wd["D"]), "bf16", 200 + nb)
-        qn, kn, vn = (synth.to_numpy_exact(t) for t in (q, k, v))
-        t0 = time.perf_counter()
-        oracle.decode(qn, kn, vn, synth.default_scale(wd["D"]))
-        td += time.perf_counter() - t0
-        kv_bytes += 2.0 * wd["Hkv"] * wd["Sk"] * wd["D"] * 2
-        nb += 1
-    tflops = flops / tp / 1e12
-    gbs = kv_bytes / td / 1e9
-    value = 100.0 * 0.5 * (tflops / PEAK_BF16_TFLOPS + gbs / PEAK_HBM_GBS)
-    del np, torch
+    return blas, threads
+
+
+def _oracle_slabs(name: str, w):
+    """Slabs of a workload the fp64 oracle runs one at a time, each a tuple
+    (q, k, v, call-args) of device tensors: one batch row per slab for the
+    prefills and the batched decode, one kv head (with its query heads) for the
+    long decode, so host memory stays near one slab (about 2 GiB in fp64)."""
+    if w["kind"] == "prefill":
+        for b in range(w["B"]):
+            yield w["q"][b:b + 1], w["k"][b:b + 1], w["v"][b:b + 1]
+    elif w["B"] > 1:
+        for b in range(w["B"]):
+            yield w["q"][b:b + 1], w["k"][b:b + 1], w["v"][b:b + 1]
+    else:
+        G = w["Hq"] // w["Hkv"]
+        for g in range(w["Hkv"]):
+            yield (w["q"][:, g * G:(g + 1) * G], w["k"][:, g:g + 1], w["v"][:, g:g + 1])
+
+
+def cpu_baseline(dev):
+    """The fp64 oracle, untuned, on every workload in full: each workload's
+    own seeded inputs (the ones the GPU computes on), copied to the host one
+    slab at a time; only the oracle calls are timed (time.perf_counter)."""
+    import torch
+
+    import oracle
+    from exact_attention_33_amd import synth
+
+    blas, threads = _blas_info()
+    per = {}
+    for name in synth.WORKLOADS:
+        w = synth.workload_inputs(name, dev)
+        secs = 0.0
+        for q, k, v in _oracle_slabs(name, w):
+            qn, kn, vn = (synth.to_numpy_exact(t) for t in (q, k, v))
+            t0 = time.perf_counter()
+            if w["kind"] == "prefill":
+                oracle.attention(qn, kn, vn, w["scale"], bool(w["causal"]), w["window"])
+            else:
+                oracle.decode(qn, kn, vn, w["scale"])
+            secs += time.perf_counter() - t0
+            del qn, kn, vn
+        if w["kind"] == "prefill":
+            fl = (window_flops(w) if w["window"] >= 0 else
+                  prefill_flops(w) if w["causal"] else 4.0 * w["D"] * w["Sq"] * w["Sk"] * w["B"] * w["Hq"])
+            per[name] = {"seconds": round(secs, 3), "gflops": round(fl / secs / 1e9, 3),
+                         "algorithmic_flops": fl}
+        else:
+            kv = decode_kv_bytes(w)
+            per[name] = {"seconds": round(secs, 3), "kv_gbs": round(kv / secs / 1e9, 3),
+                         "algorithmic_bytes": kv}
+        del w
+        torch.cuda.empty_cache()
+    p_tflops = per[PREFILL]["gflops"] / 1e3
+    d_gbs = per[DECODE]["kv_gbs"]
+    value = 100.0 * 0.5 * (p_tflops / PEAK_BF16_TFLOPS + d_gbs / PEAK_HBM_GBS)
+    total = sum(e["seconds"] for e in per.values())
     return {
         "value": value, "unit": "% of MI355X peak (mean of prefill MFMA and decode HBM fractions)",
         "cores": threads, "kind": "oracle",
-        "sample": (f"fp64 numpy oracle, timed per call: causal prefill on {nh} of 64 heads (S=2048, D=128) took "
-                   f"{tp:.2f} s -> {tflops * 1e3:.2f} GFLOP/s; decode on {nb} of 16 batch rows "
-                   f"(Hq=32, Hkv=8, Sk=32768) took {td:.2f} s -> {gbs:.2f} GB/s of bf16 KV"),
-        "prefill_gflops": tflops * 1e3, "decode_gbs": gbs,
+        "sample": (f"fp64 numpy oracle, one full wall-clock run of each of the five workloads on their own "
+                   f"seeded inputs ({total:.1f} s of oracle time in all; slabs of one batch row, or one kv "
+                   f"head for the long decode, copied to the host one at a time); value from the causal "
+                   f"prefill ({per[PREFILL]['gflops']:.1f} GFLOP/s) and the GQA decode "
+                   f"({d_gbs:.2f} GB/s of bf16 KV)"),
+        "per_config": per,
         "affinity_cores": len(os.sched_getaffinity(0)), "blas": blas, "cpu_model": cpu_model(),
     }
 
@@ -251,6 +276,30 @@ def other_configs(dev, ach, iters: int = 50):
 
     out = {}
     stream = torch.cuda.current_stream(dev)
+    # the tiny fp32 workload is launch-latency bound: per-launch GPU time by
+    # events, and the host's round trip (enqueue, then wait for completion)
+    wt = synth.workload_inputs("tiny_f32", dev)
+    ot = torch.empty_like(wt["q"])
+    lt = torch.empty(wt["B"], wt["Hq"], wt["Sq"], dtype=torch.float32, device=dev)
+
+    def run_t(i):
+        ops.attn_fwd_f32(wt["q"], wt["k"], wt["v"], causal=False, scale=wt["scale"], out=ot, lse=lt)
+
+    st_ev = launch_stats(time_launches(run_t, 200, stream))
+    rt = []
+    for _ in range(200):
+        t0 = time.perf_counter()
+        run_t(0)
+        torch.cuda.synchronize()
+        rt.append((time.perf_counter() - t0) * 1e3)
+    out["tiny_f32"] = {
+        "shape": {k: wt[k] for k in ("B", "Hq", "Sq", "Sk", "D")}, "dtype": "f32", "bound": "latency",
+        "gpu_launch_ms": st_ev, "host_roundtrip_ms": launch_stats(rt),
+        "algorithmic_flops": 4.0 * wt["D"] * wt["Sq"] * wt["Sk"],
+        "note": "gpu_launch_ms: HIP events around each launch; host_roundtrip_ms: the call plus "
+                "torch.cuda.synchronize(), wall clock",
+    }
+    del wt, ot, lt
     ww = synth.workload_inputs("window_encoder", dev)
     copies = []
     for c in range(3):
@@ -534,6 +583,18 @@ def main():
         prefill()
         decode()
     torch.cuda.synchronize()
+    # However few --warmup steps were asked for, the timed steps start only
+    # after WARM_MS of continuous GPU work: the clock takes tens of
+    # milliseconds of load to ramp (the same prefill measured 102 us cold and
+    # 82 us warm).  Every other series gets the same in time_launches().
+    t_w0, warm_pairs = time.perf_counter(), 0
+    while (time.perf_counter() - t_w0) * 1e3 < WARM_MS:
+        for _ in range(4):
+            prefill()
+            decode()
+            warm_pairs += 1
+        torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - t_w0) * 1e3
 
     # Timed region: K steps of work (K prefills, then K decodes), each launch
     # bracketed by HIP events on the stream it runs on.  Running each kernel
@@ -590,6 +651,7 @@ def main():
         "value": round(value, 3),
         "unit": "% of MI355X peak (mean of prefill MFMA and decode HBM fractions)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "warm_ms": round(warm_ms, 1), "warm_steps_busy": warm_pairs,
         "ms_per_step": round(step_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
@@ -628,7 +690,7 @@ def main():
     }
     line["other_configs"] = other_configs(dev, ach)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline()
+        line["cpu_baseline"] = cpu_baseline(dev)
     print(json.dumps(line), flush=True)
 
 

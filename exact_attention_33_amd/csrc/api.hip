@@ -25,6 +25,12 @@ int check_common(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
   return ATTN_OK;
 }
 
+// The kernels move q, k, v, o (and the gradients) in 16-byte vectors and
+// lse, delta and the decode workspace in 4- and 16-byte words.
+bool misaligned(const void* p, uintptr_t bytes) {
+  return p != nullptr && ((uintptr_t)p % bytes) != 0;
+}
+
 int check_scale(float scale) {
   return (isfinite(scale) && scale > 0.f) ? ATTN_OK : ATTN_ERR_ARG;
 }
@@ -41,6 +47,8 @@ int check_fwd(const void* q, const void* k, const void* v, const void* o, int B,
   if (rows == 0) return ATTN_OK;  // nothing to read or write
   if (q == nullptr || o == nullptr) return ATTN_ERR_NULL;
   if (Sk > 0 && (k == nullptr || v == nullptr)) return ATTN_ERR_NULL;
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16))
+    return ATTN_ERR_ARG;
   const int64_t bh = (int64_t)B * Hq;
   if (bh > INT32_MAX / 8) return ATTN_ERR_SHAPE;
   if (((int64_t)Sq + 63) / 64 * bh > INT32_MAX) return ATTN_ERR_SHAPE;  // grid size
@@ -57,6 +65,8 @@ int check_decode(const void* q, const void* kc, const void* vc, const void* o, i
   if (bh == 0) return ATTN_OK;
   if (q == nullptr || o == nullptr) return ATTN_ERR_NULL;
   if (Sk > 0 && (kc == nullptr || vc == nullptr)) return ATTN_ERR_NULL;
+  if (misaligned(q, 16) || misaligned(kc, 16) || misaligned(vc, 16) || misaligned(o, 16))
+    return ATTN_ERR_ARG;
   const int64_t nhg = ((Hq / Hkv) + 15) / 16;
   if ((int64_t)num_splits * Hkv * B * nhg > INT32_MAX) return ATTN_ERR_SHAPE;
   if (bh * ((int64_t)num_splits + 255) / 256 * (D / 64) > INT32_MAX) return ATTN_ERR_SHAPE;
@@ -132,7 +142,8 @@ const char* attn_error_string(int status) {
     case ATTN_ERR_WINDOW: return "ATTN_ERR_WINDOW: window must be -1 or a half width >= 0";
     case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace missing or too small";
     case ATTN_ERR_HIP: return "ATTN_ERR_HIP: the HIP runtime reported an error";
-    case ATTN_ERR_ARG: return "ATTN_ERR_ARG: causal must be 0/1 and scale finite and > 0";
+    case ATTN_ERR_ARG:
+      return "ATTN_ERR_ARG: causal must be 0/1, scale finite and > 0, tensors 16-byte and lse 4-byte aligned";
     default: return "unknown attn status";
   }
 }
@@ -144,6 +155,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
              hipStream_t stream) {
   int st = check_fwd(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, window, scale);
   if (st != ATTN_OK || (int64_t)B * Hq * Sq == 0) return st;
+  if (misaligned(lse, 4)) return ATTN_ERR_ARG;
   return to_status(ea::launch_fwd_bf16((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                                        (uint16_t*)o, lse,
                                        fwd_shape(B, Hq, Hkv, Sq, Sk, D, causal, window, scale),
@@ -155,6 +167,7 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
                  hipStream_t stream) {
   int st = check_fwd(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, window, scale);
   if (st != ATTN_OK || (int64_t)B * Hq * Sq == 0) return st;
+  if (misaligned(lse, 4)) return ATTN_ERR_ARG;
   return to_status(ea::launch_fwd_f32(q, k, v, o, lse,
                                       fwd_shape(B, Hq, Hkv, Sq, Sk, D, causal, window, scale),
                                       stream));
@@ -169,6 +182,7 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o, float*
       check_scale(v_descale) != ATTN_OK)
     return ATTN_ERR_ARG;
   if ((int64_t)B * Hq * Sq == 0) return ATTN_OK;
+  if (misaligned(lse, 4)) return ATTN_ERR_ARG;
   return to_status(ea::launch_fwd_fp8((const uint8_t*)q8, (const uint8_t*)k8, (const uint8_t*)v8,
                                       (uint16_t*)o, lse,
                                       fwd_shape(B, Hq, Hkv, Sq, Sk, D, causal, window, scale),
@@ -187,6 +201,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     return ATTN_ERR_NULL;
   if (keys > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
     return ATTN_ERR_NULL;
+  if (misaligned(dout, 16) || misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16) ||
+      misaligned(lse, 4) || misaligned(delta, 4))
+    return ATTN_ERR_ARG;
   if (((int64_t)Sk + 127) / 128 * B * Hkv > INT32_MAX) return ATTN_ERR_SHAPE;  // grid size
   return to_status(ea::launch_bwd((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                                   (const uint16_t*)o, (const uint16_t*)dout, lse, (uint16_t*)dq,
@@ -201,6 +218,7 @@ int attn_decode_ex(const void* q, const void* kcache, const void* vcache, void* 
   if (st != ATTN_OK || (int64_t)B * Hq == 0) return st;
   if (workspace == nullptr || workspace_bytes < attn_decode_workspace_bytes(B, Hq, D, num_splits))
     return ATTN_ERR_WORKSPACE;
+  if (misaligned(lse, 4) || misaligned(workspace, 16)) return ATTN_ERR_ARG;
   ea::DecodeShape s;
   s.B = B;
   s.Hq = Hq;

@@ -18,7 +18,7 @@ struct FwdShape {
 hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                            float* lse, const FwdShape& s, hipStream_t stream);
 
-// Prefill on fp8 (e4m3) codes with per-tensor descales, bf16 o, D = 128; one launch.
+// Prefill on fp8 (e4m3) codes with per-tensor descales, bf16 o, D = 64 or 128; one launch.
 hipError_t launch_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, uint16_t* o, float* lse,
                           const FwdShape& s, float q_descale, float k_descale, float v_descale,
                           hipStream_t stream);

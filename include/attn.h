@@ -26,8 +26,11 @@
  *     k, v   [B, Hkv, Sk, D]     (decode: the KV cache, same shape)
  *     lse    [B, Hq,  Sq] fp32   (decode: [B, Hq])
  * Device pointers only (memory from hipMalloc or a framework allocator on the
- * current device).  The caller owns every buffer; the library never frees or
- * keeps a caller pointer after the call returns.
+ * current device).  The kernels move whole 16-byte vectors: q, k, v, o, the
+ * gradient tensors and the decode workspace must start on a 16-byte
+ * boundary, lse and delta on a 4-byte boundary (ATTN_ERR_ARG otherwise).
+ * The caller owns every buffer; the library never frees or keeps a caller
+ * pointer after the call returns.
  *
  * Execution: every call only enqueues work on `stream` (NULL = the default
  * stream) and returns; there is no host synchronisation.  Arguments are
@@ -55,7 +58,8 @@ typedef enum {
   ATTN_ERR_WINDOW = 6,    /* window < -1                                                 */
   ATTN_ERR_WORKSPACE = 7, /* workspace NULL or smaller than attn_decode_workspace_bytes */
   ATTN_ERR_HIP = 8,       /* the HIP runtime reported an error (launch, allocation)      */
-  ATTN_ERR_ARG = 9        /* causal not 0/1, or scale not finite and > 0                 */
+  ATTN_ERR_ARG = 9        /* causal not 0/1, scale not finite and > 0, or a pointer     */
+                          /* misaligned (see "Layout" above)                           */
 } attn_status;
 
 /*

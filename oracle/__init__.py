@@ -57,7 +57,6 @@ from .attention import (  # noqa: F401
     merge,
     combine,
     finish,
-    n_visible,
 )
 from .backward import attention_backward  # noqa: F401
 from .fp8 import E4M3_MAX, attention_fp8, e4m3_decode  # noqa: F401

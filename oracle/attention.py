@@ -256,9 +256,3 @@ def finish(part):
     o = np.where(live[:, None], acc / np.where(live, l, 1.0)[:, None], 0.0)
     lse = np.where(live, m + np.log(np.where(live, l, 1.0)), NEG_INF)
     return o, lse
-
-
-def n_visible(i: int, Sq: int, Sk: int, causal: bool, window: int) -> int:
-    """Count of keys visible to query ``i``, by direct enumeration (small sizes)."""
-    return int(visibility([i], Sq, Sk, causal, window).sum())
-

@@ -149,3 +149,30 @@ def test_fwd_fp8_validation(L):
     assert call(vd=float("inf")) == ARG
     assert call(q=None) == NULL
     assert call(q=None, Sq=0) == OK          # nothing to compute
+
+
+def test_misaligned_pointers_are_rejected(L):
+    odd = ctypes.c_void_p(0x1008)      # 8-byte aligned, not 16
+    odd4 = ctypes.c_void_p(0x1002)     # not 4-byte aligned
+    for f32 in (False, True):
+        for name in ("q", "k", "v", "o"):
+            assert fwd(L, f32=f32, **{name: odd}) == ARG, name
+        assert fwd(L, f32=f32, lse=odd4) == ARG
+    f = ctypes.c_float
+    assert L.attn_fwd_fp8(odd, FAKE, FAKE, FAKE, None, 1, 2, 1, 8, 8, 128, 0, -1, f(0.125),
+                          f(1.0), f(1.0), f(1.0), None) == ARG
+    for name in ("q", "k", "v", "o"):
+        assert dec_ex(L, **{name: odd}) == ARG, name
+    assert dec_ex(L, lse=odd4) == ARG
+    assert dec_ex(L, ws=odd) == ARG
+
+    def bwd(**kw):
+        p = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, delta=FAKE)
+        p.update(kw)
+        return L.attn_bwd(p["q"], p["k"], p["v"], p["o"], p["do"], p["lse"], p["dq"], p["dk"], p["dv"],
+                          p["delta"], 1, 2, 1, 8, 8, 64, 0, -1, ctypes.c_float(0.125), None)
+
+    for name in ("q", "k", "v", "o", "do", "dq", "dk", "dv"):
+        assert bwd(**{name: odd}) == ARG, name
+    for name in ("lse", "delta"):
+        assert bwd(**{name: odd4}) == ARG, name

@@ -82,3 +82,25 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_oracle_slabs_cover_each_workload_once():
+    import torch
+    # prefill: one batch row per slab
+    w = dict(kind="prefill", B=3, Hq=4, Hkv=2, q=torch.arange(3 * 4 * 5 * 2).reshape(3, 4, 5, 2),
+             k=torch.zeros(3, 2, 5, 2), v=torch.zeros(3, 2, 5, 2))
+    slabs = list(bench._oracle_slabs("p", w))
+    assert len(slabs) == 3 and torch.equal(torch.cat([s[0] for s in slabs]), w["q"])
+    # batched decode: one batch row per slab
+    w = dict(kind="decode", B=2, Hq=4, Hkv=2, q=torch.randn(2, 4, 8), k=torch.randn(2, 2, 6, 8),
+             v=torch.randn(2, 2, 6, 8))
+    slabs = list(bench._oracle_slabs("d", w))
+    assert len(slabs) == 2 and torch.equal(torch.cat([s[1] for s in slabs]), w["k"])
+    # one batch row: one kv head and its query heads per slab
+    w = dict(kind="decode", B=1, Hq=8, Hkv=2, q=torch.randn(1, 8, 8), k=torch.randn(1, 2, 6, 8),
+             v=torch.randn(1, 2, 6, 8))
+    slabs = list(bench._oracle_slabs("l", w))
+    assert len(slabs) == 2
+    assert torch.equal(torch.cat([s[0] for s in slabs], dim=1), w["q"])
+    assert torch.equal(torch.cat([s[2] for s in slabs], dim=1), w["v"])
+    assert all(s[0].shape[1] == 4 and s[1].shape[1] == 1 for s in slabs)

@@ -40,8 +40,8 @@ MUTANTS = {
     "online alpha inverted": ("alpha = np.where(np.isfinite(m), np.exp(m - m_ref), 0.0)",
                               "alpha = np.where(np.isfinite(m), np.exp(m_ref - m), 0.0)"),
     "online keeps stale max": ("                m = m_new\n", "                m = np.maximum(m, 0.0)\n"),
-    "finish misses max": ("lse = np.where(live, m + np.log(np.where(live, l, 1.0)), NEG_INF)\n    return o, lse\n\n\ndef n_visible",
-                          "lse = np.where(live, np.log(np.where(live, l, 1.0)), NEG_INF)\n    return o, lse\n\n\ndef n_visible"),
+    "finish misses max": ("lse = np.where(live, m + np.log(np.where(live, l, 1.0)), NEG_INF)",
+                          "lse = np.where(live, np.log(np.where(live, l, 1.0)), NEG_INF)"),
     "balanced tree drops odd leaf": ("            if len(parts) % 2:\n                nxt.append(parts[-1])\n",
                                      "            pass\n"),
 }
