@@ -43,6 +43,11 @@ DECODE = "gqa_decode"
 KERNEL_SOURCES = ["fwd_bf16.hip", "fwd_fp8.hip", "decode.hip", "bwd.hip", "common.h"]
 
 
+def progress(msg: str):
+    """One line per finished phase on stderr (stdout carries only the JSON line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def visible_pairs_causal(Sq: int, Sk: int) -> int:
     """Number of (query, key) pairs a bottom-right causal mask keeps."""
     off = Sk - Sq
@@ -224,6 +229,7 @@ def cpu_baseline(dev):
                 oracle.decode(qn, kn, vn, w["scale"])
             secs += time.perf_counter() - t0
             del qn, kn, vn
+        progress(f"cpu oracle {name}: {secs:.2f} s")
         if w["kind"] == "prefill":
             fl = (window_flops(w) if w["window"] >= 0 else
                   prefill_flops(w) if w["causal"] else 4.0 * w["D"] * w["Sq"] * w["Sk"] * w["B"] * w["Hq"])
@@ -637,7 +643,9 @@ def main():
     ip_avg = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
     id_avg = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
 
+    progress(f"timed steps done: prefill {p_avg * 1e3:.1f} us, decode {d_avg * 1e3:.1f} us per launch")
     ach = achievable(dev)
+    progress("achievable rates done")
     flops = prefill_flops(wp)
     kv = decode_kv_bytes(wd)
     p_tflops = flops / (p_avg * 1e-3) / 1e12
@@ -689,6 +697,7 @@ def main():
         "kernel_source_digest": source_digest(),
     }
     line["other_configs"] = other_configs(dev, ach)
+    progress("other configs done")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(dev)
     print(json.dumps(line), flush=True)

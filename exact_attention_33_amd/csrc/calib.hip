@@ -65,8 +65,35 @@ __global__ __launch_bounds__(kCalibThreads) void mfma_kernel(float* __restrict__
   if (lane == 0) out[blockIdx.x * 4 + (threadIdx.x >> 6)] = s;
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// One fp8 matrix instruction on caller-given operands, C = 0, unit block
+// scales (E4M3 x E4M3).  Lane l holds row / column l % 32 and the 32 k-values
+// 32 * (l / 32) .. + 31 of its A row and B column; result element i of lane l
+// is c[8 * (i / 4) + 4 * (l / 32) + i % 4][l % 32].
+__global__ __launch_bounds__(64) void mfma_fp8_probe_kernel(const uint8_t* __restrict__ a,
+                                                            const uint8_t* __restrict__ b,
+                                                            float* __restrict__ c) {
+  const int lane = threadIdx.x & 63;
+  const int rc = lane & 31, half = lane >> 5;
+  const i32x8 av = *(const i32x8*)(a + rc * 64 + 32 * half);
+  const i32x8 bv = *(const i32x8*)(b + rc * 64 + 32 * half);
+  f32x16 acc = {};
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) c[(8 * (i >> 2) + 4 * half + (i & 3)) * 32 + rc] = acc[i];
+}
+
 }  // namespace
 }  // namespace ea
+
+extern "C" int attn_calib_mfma_fp8(const void* a, const void* b, float* c, hipStream_t stream) {
+  if (a == nullptr || b == nullptr || c == nullptr) return ATTN_ERR_NULL;
+  if (((uintptr_t)a | (uintptr_t)b | (uintptr_t)c) % 16 != 0) return ATTN_ERR_ARG;
+  hipLaunchKernelGGL(ea::mfma_fp8_probe_kernel, dim3(1), dim3(64), 0, stream, (const uint8_t*)a,
+                     (const uint8_t*)b, c);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
 
 extern "C" int attn_calib_stream(const void* src, size_t src_bytes, void* dst, size_t dst_bytes,
                                  hipStream_t stream) {

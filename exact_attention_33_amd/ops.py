@@ -25,7 +25,7 @@ STATUS_NAMES = {
 # every symbol include/attn.h and include/attn_calib.h declare
 EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_fp8", "attn_bwd", "attn_decode", "attn_decode_ex",
            "attn_decode_workspace_bytes", "attn_error_string", "attn_version",
-           "attn_calib_stream", "attn_calib_mfma", "attn_calib_mfma_flops")
+           "attn_calib_stream", "attn_calib_mfma", "attn_calib_mfma_flops", "attn_calib_mfma_fp8")
 
 _lib = None
 
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
     L.attn_calib_mfma.restype = i
     L.attn_calib_mfma_flops.argtypes = [i, i]
     L.attn_calib_mfma_flops.restype = ctypes.c_double
+    L.attn_calib_mfma_fp8.argtypes = [vp, vp, vp, vp]
+    L.attn_calib_mfma_fp8.restype = i
     _lib = L
     return L
 
@@ -281,6 +283,18 @@ def calib_stream(src: torch.Tensor, dst: torch.Tensor):
     _check(lib().attn_calib_stream(_ptr(src), src.numel() * src.element_size(), _ptr(dst),
                                    dst.numel() * dst.element_size(), _stream(dst)))
     return dst
+
+
+def calib_mfma_fp8(a: torch.Tensor, b: torch.Tensor) -> torch.Tensor:
+    """One fp8 (E4M3) matrix instruction: ``c[m, n] = sum_k a[m, k] * b[n, k]`` as the
+    matrix core sums it; ``a, b`` are 32 x 64 uint8 codes on the GPU."""
+    for t, n in ((a, "a"), (b, "b")):
+        _want(t, n, torch.uint8, 2, a.device)
+        if tuple(t.shape) != (32, 64):
+            raise ValueError(f"{n} must be 32 x 64 codes")
+    c = torch.empty(32, 32, dtype=torch.float32, device=a.device)
+    _check(lib().attn_calib_mfma_fp8(_ptr(a), _ptr(b), _ptr(c), _stream(c)))
+    return c
 
 
 def calib_mfma(out: torch.Tensor, workgroups: int, iters: int) -> float:

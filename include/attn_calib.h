@@ -49,6 +49,16 @@ int attn_calib_mfma(float* out, int workgroups, int iters, hipStream_t stream);
 /* 2 * 32 * 32 * 16 flops per instruction * 4 chains * 4 wavefronts * iters * workgroups. */
 double attn_calib_mfma_flops(int workgroups, int iters);
 
+/* One v_mfma_scale_f32_32x32x64_f8f6f4 instruction (OCP E4M3 x E4M3 operands,
+ * block scales 2^0, zero accumulator) on one wavefront:
+ *     c[m][n] = sum_{k<64} e4m3(a[m][k]) * e4m3(b[n][k])   as the matrix core sums it.
+ *   a, b: 32 x 64 byte codes, row-major (row m of a, row n of b hold the 64
+ *         k-values); c: 32 x 32 fp32, row-major.  All 16-byte aligned.
+ * The fp8 prefill computes its scores with this instruction; this call lets a
+ * test observe the instruction's own accumulation error on constructed inputs.
+ * Errors: ATTN_ERR_NULL, ATTN_ERR_ARG (misaligned), ATTN_ERR_HIP. */
+int attn_calib_mfma_fp8(const void* a, const void* b, float* c, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
