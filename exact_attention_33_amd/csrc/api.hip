@@ -121,6 +121,30 @@ int library_workspace(size_t need, void** out) {
   return ATTN_OK;
 }
 
+// Scratch memory of attn_decode_noalloc: a static device array, one copy per
+// GPU the library runs on, held until the process ends.  Host code never
+// names `scratch` as an address: the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kNoAllocBytes = ATTN_DECODE_NOALLOC_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};  // per device: the address of `scratch` on it
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return ATTN_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -230,6 +254,20 @@ int attn_decode_ex(const void* q, const void* kcache, const void* vcache, void* 
   return to_status(ea::launch_decode((const uint16_t*)q, (const uint16_t*)kcache,
                                      (const uint16_t*)vcache, (uint16_t*)o, lse, s,
                                      (float*)workspace, stream));
+}
+
+int attn_decode_noalloc(const void* q, const void* kcache, const void* vcache, void* o, float* lse,
+                        int B, int Hq, int Hkv, int Sk, int D, int num_splits, float scale,
+                        hipStream_t stream) {
+  int st = check_decode(q, kcache, vcache, o, B, Hq, Hkv, Sk, D, num_splits, scale);
+  if (st != ATTN_OK || (int64_t)B * Hq == 0) return st;
+  const size_t need = attn_decode_workspace_bytes(B, Hq, D, num_splits);
+  if (need > kNoAllocBytes) return ATTN_ERR_WORKSPACE;
+  if (misaligned(lse, 4)) return ATTN_ERR_ARG;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != ATTN_OK) return st;
+  return attn_decode_ex(q, kcache, vcache, o, lse, B, Hq, Hkv, Sk, D, num_splits, scale, ws, need,
+                        stream);
 }
 
 int attn_decode(const void* q, const void* kcache, const void* vcache, void* o, int B, int Hq,

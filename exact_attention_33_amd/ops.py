@@ -24,6 +24,7 @@ STATUS_NAMES = {
 }
 # every symbol include/attn.h and include/attn_calib.h declare
 EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_fp8", "attn_bwd", "attn_decode", "attn_decode_ex",
+           "attn_decode_noalloc",
            "attn_decode_workspace_bytes", "attn_error_string", "attn_version",
            "attn_calib_stream", "attn_calib_mfma", "attn_calib_mfma_flops", "attn_calib_mfma_fp8")
 
@@ -58,6 +59,8 @@ def lib() -> ctypes.CDLL:
     L.attn_decode.restype = i
     L.attn_decode_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     L.attn_decode_ex.restype = i
+    L.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    L.attn_decode_noalloc.restype = i
     L.attn_decode_workspace_bytes.argtypes = [i, i, i, i]
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_error_string.argtypes = [i]
@@ -269,6 +272,25 @@ def attn_decode_ex(q, kcache, vcache, num_splits, scale=None, out=None, lse=None
         _check(lib().attn_decode_ex(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(o), _ptr(lse), B, Hq, Hkv,
                                     Sk, D, int(num_splits), scale, _ptr(workspace), workspace.numel(),
                                     _stream(q)))
+    return o, lse
+
+
+NOALLOC_BYTES = 32 << 20   # ATTN_DECODE_NOALLOC_BYTES
+
+
+def attn_decode_noalloc(q, kcache, vcache, num_splits, out, lse=None, scale=None):
+    """Split-KV decode whose partials live in the library's static device array
+    (no device allocation by the library; ``out`` and the optional ``lse`` are
+    the caller's) -> ``(o, lse)``."""
+    B, Hq, Hkv, Sk, D, o = _decode_shapes(q, kcache, vcache, out)
+    if lse is not None:
+        _want(lse, "lse", torch.float32, 2, q.device)
+        if tuple(lse.shape) != (B, Hq):
+            raise ValueError("lse must be [B, Hq]")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    with torch.cuda.device(q.device):  # kernels launch on the current device
+        _check(lib().attn_decode_noalloc(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(o), _ptr(lse), B, Hq,
+                                         Hkv, Sk, D, int(num_splits), scale, _stream(q)))
     return o, lse
 
 

@@ -166,6 +166,30 @@ int attn_decode_ex(const void* q, const void* kcache, const void* vcache, void* 
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: attn_decode_ex
+ * without a workspace argument.  The partials go to a static device array of
+ * ATTN_DECODE_NOALLOC_BYTES inside the library (one per GPU, held until the
+ * process ends); the call itself allocates nothing.
+ *
+ *   Arguments and results as attn_decode_ex.  ATTN_ERR_WORKSPACE when
+ *   attn_decode_workspace_bytes(B, Hq, D, num_splits) exceeds
+ *   ATTN_DECODE_NOALLOC_BYTES (32 MiB: e.g. B*Hq = 512 rows at D = 128 with
+ *   up to 125 splits, or one row with up to 64 K splits).
+ * The array needs no clearing (every partial is written before it is read)
+ * and keeps whatever the last call left in it.  All calls on one GPU share
+ * it: calls that overlap in time on one GPU (two streams, two threads) race
+ * and corrupt each other's partials -- serialise them, or use attn_decode_ex
+ * with one workspace per stream.  The first call on a device looks up the
+ * array's device address (no allocation); that lookup fails with
+ * ATTN_ERR_HIP if the library's code object cannot be loaded on the device.
+ */
+#define ATTN_DECODE_NOALLOC_BYTES ((size_t)32 << 20)
+int attn_decode_noalloc(const void* q, const void* kcache, const void* vcache, void* o, float* lse,
+                        int B, int Hq, int Hkv, int Sk, int D, int num_splits, float scale,
+                        hipStream_t stream);
+
+/*
  * Workspace bytes attn_decode_ex needs: one fp32 (m, l, acc[D]) partial per
  * (b, h, chunk), B*Hq*num_splits*(D+2)*4, plus room for the upper tree levels
  * when num_splits exceeds the 256 partials one combine workgroup merges.

@@ -176,3 +176,19 @@ def test_misaligned_pointers_are_rejected(L):
         assert bwd(**{name: odd}) == ARG, name
     for name in ("lse", "delta"):
         assert bwd(**{name: odd4}) == ARG, name
+
+
+def test_noalloc_decode_validation(L):
+    def call(B=2, Hq=8, Hkv=2, Sk=100, D=128, ns=4, q=FAKE, lse=None, scale=0.088):
+        return L.attn_decode_noalloc(q, FAKE, FAKE, FAKE, lse, B, Hq, Hkv, Sk, D, ns, scale, None)
+
+    assert call(q=None) == NULL
+    assert call(ns=0) == SPLITS
+    assert call(D=96) == HEADDIM
+    assert call(scale=0.0) == ARG
+    assert call(lse=ctypes.c_void_p(0x1002)) == ARG
+    assert call(q=None, B=0) == OK
+    # partials beyond the 32 MiB static array: refused before any HIP call
+    assert L.attn_decode_workspace_bytes(64, 32, 128, 64) > ops.NOALLOC_BYTES
+    assert call(B=64, Hq=32, Hkv=8, Sk=1024, ns=64) == WORKSPACE
+    assert L.attn_decode_workspace_bytes(16, 32, 128, 64) <= ops.NOALLOC_BYTES
