@@ -2,11 +2,16 @@
 // matrix cores, nothing rounded to bf16), online softmax in base 2, the same
 // causal / sliding-window / GQA semantics as the bf16 kernel.
 //
-// One workgroup = 2 wavefronts = 64 query rows of one (b, h).  Each query row
-// is owned by a lane pair (lane, lane ^ 32): each lane keeps half of the row's
-// dimensions of q and of the output accumulator in registers; a dot product
-// is the sum of the two halves (one lane swap).  K and V tiles of 32 keys are
-// staged in LDS (every lane of a half reads the same address: broadcast).
+// Built for latency (the fp32 workload is a single 128 x 128 head): one
+// workgroup = NW = 8 wavefronts serving 32 query rows of one (b, h).  Each query
+// row is owned by a lane pair (lane, lane ^ 32) in every wavefront: each lane
+// keeps half of the row's dimensions of q and of its accumulator, and a dot
+// product is the sum of the two halves (one lane swap).  K and V blocks of KT
+// keys are staged in LDS by the whole workgroup; wavefront w takes keys
+// w, w + NW, ... of each block, so all NW wavefronts work on every block at
+// once.  At the end the NW partial results (m, l, acc) of each row are merged
+// through LDS with the log-sum-exp operator -- the merge of the Tree Attention
+// abstract (express24.ir page), here across the wavefronts of one workgroup.
 #include "common.h"
 #include "kernels.h"
 
@@ -25,14 +30,19 @@ struct F32Args {
   int n_qtiles;
 };
 
-constexpr int kRows = 64;
-constexpr int kTile = 32;
+constexpr int kRows = 32;  // query rows per workgroup
 
-template <int D>
-__global__ __launch_bounds__(128) void fwd_f32_kernel(F32Args a) {
-  constexpr int DH = D / 2;  // dimensions per lane
-  __shared__ __attribute__((aligned(16))) float sK[kTile * D];
-  __shared__ __attribute__((aligned(16))) float sV[kTile * D];
+template <int D, int kNW>
+__global__ __launch_bounds__(64 * kNW) void fwd_f32_kernel(F32Args a) {
+  constexpr int DH = D / 2;                 // dimensions per lane
+  constexpr int KT = (D == 64) ? 128 : 64;  // keys per LDS block (64 KB of K and V)
+  constexpr int MS = D + 4;                 // floats per (row, wavefront) partial, 16-byte rows
+  static_assert(KT % kNW == 0, "whole keys per wavefront");
+  // K/V blocks during the loop, the partials of the merge afterwards
+  constexpr int NF = (2 * KT * D > kNW * kRows * MS) ? 2 * KT * D : kNW * kRows * MS;
+  __shared__ __attribute__((aligned(16))) float smem[NF];
+  float* sK = smem;
+  float* sV = smem + KT * D;
 
   const int BH = a.B * a.Hq;
   const int bh = blockIdx.x % BH;
@@ -40,7 +50,7 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(F32Args a) {
   const int b = bh / a.Hq, h = bh % a.Hq;
   const int g = h / (a.Hq / a.Hkv);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hh = lane >> 5;
+  const int hh = lane >> 5, l32 = lane & 31;
   const int off = a.Sk - a.Sq;
   const int w = a.window;
 
@@ -55,25 +65,36 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(F32Args a) {
 
   const size_t q_base = ((size_t)b * a.Hq + h) * (size_t)a.Sq;
   const size_t kv_base = ((size_t)b * a.Hkv + g) * (size_t)a.Sk;
-  const int qi = r0 + wave * 32 + (lane & 31);
+  const int qi = r0 + l32;
   const bool q_ok = qi < a.Sq;
   const int pos = qi + off;
+  int key_lo = 0, key_hi = a.Sk - 1;  // keys this row sees
+  if (a.causal) key_hi = min(key_hi, pos);
+  if (w >= 0) {
+    key_lo = max(key_lo, pos - w);
+    key_hi = min(key_hi, pos + w);
+  }
 
   float qv[DH], acc[DH];
   {
     const float* qrow = a.q + (q_base + (q_ok ? qi : 0)) * D + hh * DH;
 #pragma unroll
-    for (int d = 0; d < DH; ++d) {
-      qv[d] = q_ok ? qrow[d] : 0.f;
-      acc[d] = 0.f;
+    for (int d = 0; d < DH; d += 4) {
+      const f32x4 x = q_ok ? *(const f32x4*)(qrow + d) : f32x4{0, 0, 0, 0};
+      qv[d] = x[0];
+      qv[d + 1] = x[1];
+      qv[d + 2] = x[2];
+      qv[d + 3] = x[3];
     }
+#pragma unroll
+    for (int d = 0; d < DH; ++d) acc[d] = 0.f;
   }
-  float m_run = kNegInf, l_run = 0.f;
+  float m_run = kNegInf, l_run = 0.f;  // base-2 units
   const float c2 = a.c2;
 
-  for (int kt = (kv_hi > kv_lo ? kv_lo : kv_hi); kt < kv_hi; kt += kTile) {
-    // stage keys [kt, kt + kTile) of k and v
-    for (int e = tid; e < kTile * D / 4; e += 128) {
+  for (int kt = (kv_hi > kv_lo ? kv_lo : kv_hi); kt < kv_hi; kt += KT) {
+    // stage keys [kt, kt + KT) of k and v (zeros past kv_hi)
+    for (int e = tid; e < KT * D / 4; e += 64 * kNW) {
       const int row = e / (D / 4), c4 = e % (D / 4);
       const int key = kt + row;
       f32x4 kk = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
@@ -86,19 +107,20 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(F32Args a) {
     }
     __syncthreads();
 
-    float s[kTile];
+    // this wavefront's keys of the block: kt + wave + kNW * j
+    constexpr int NJ = KT / kNW;
+    float s[NJ];
     float mx = kNegInf;
 #pragma unroll
-    for (int j = 0; j < kTile; ++j) {
-      const float* kr = sK + j * D + hh * DH;
+    for (int j = 0; j < NJ; ++j) {
+      const int row = wave + kNW * j;
+      const float* kr = sK + row * D + hh * DH;
       float part = 0.f;
 #pragma unroll
       for (int d = 0; d < DH; ++d) part = __builtin_fmaf(qv[d], kr[d], part);
-      float dot = part + xor_shfl(part, 32);
-      const int key = kt + j;
-      bool vis = key < kv_hi;
-      if (a.causal) vis = vis && key <= pos;
-      if (w >= 0) vis = vis && key >= pos - w && key <= pos + w;
+      const float dot = part + xor_shfl(part, 32);
+      const int key = kt + row;
+      const bool vis = (key < kv_hi) & (key >= key_lo) & (key <= key_hi);
       s[j] = vis ? dot * c2 : kNegInf;
       mx = fmaxf(mx, s[j]);
     }
@@ -109,10 +131,10 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(F32Args a) {
 #pragma unroll
     for (int d = 0; d < DH; ++d) acc[d] *= alpha;
 #pragma unroll
-    for (int j = 0; j < kTile; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const float p = fast_exp2(s[j] - m_use);
       rs += p;
-      const float* vr = sV + j * D + hh * DH;
+      const float* vr = sV + (wave + kNW * j) * D + hh * DH;
 #pragma unroll
       for (int d = 0; d < DH; ++d) acc[d] = __builtin_fmaf(p, vr[d], acc[d]);
     }
@@ -121,16 +143,49 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(F32Args a) {
     __syncthreads();
   }
 
-  if (q_ok) {
-    const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
-    float* orow = a.o + (q_base + qi) * D + hh * DH;
+  // merge the kNW partials of each row: partial (wave, row) at
+  // smem[(wave * kRows + row) * MS], acc[D] then m, l
+  {
+    float* pm = smem + (wave * kRows + l32) * MS;
 #pragma unroll
-    for (int d = 0; d < DH; d += 4) {
-      f32x4 ov = {acc[d] * inv, acc[d + 1] * inv, acc[d + 2] * inv, acc[d + 3] * inv};
-      *(f32x4*)(orow + d) = ov;
+    for (int d = 0; d < DH; d += 4) *(f32x4*)(pm + hh * DH + d) = f32x4{acc[d], acc[d + 1], acc[d + 2], acc[d + 3]};
+    if (hh == 0) {
+      pm[D] = m_run;
+      pm[D + 1] = l_run;
     }
-    if (a.lse != nullptr && hh == 0)
-      a.lse[q_base + qi] = (l_run > 0.f) ? (m_run + __log2f(l_run)) * kLn2 : kNegInf;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float M = kNegInf;
+#pragma unroll
+    for (int u = 0; u < kNW; ++u) M = fmaxf(M, smem[(u * kRows + l32) * MS + D]);
+    const float mref = (M == kNegInf) ? 0.f : M;
+    float out[DH], L = 0.f;
+#pragma unroll
+    for (int d = 0; d < DH; ++d) out[d] = 0.f;
+#pragma unroll
+    for (int u = 0; u < kNW; ++u) {
+      const float* pm = smem + (u * kRows + l32) * MS;
+      const float mu = pm[D];
+      const float f = (mu == kNegInf) ? 0.f : fast_exp2(mu - mref);
+      L = __builtin_fmaf(pm[D + 1], f, L);
+#pragma unroll
+      for (int d = 0; d < DH; d += 4) {
+        const f32x4 x = *(const f32x4*)(pm + hh * DH + d);
+        out[d] = __builtin_fmaf(x[0], f, out[d]);
+        out[d + 1] = __builtin_fmaf(x[1], f, out[d + 1]);
+        out[d + 2] = __builtin_fmaf(x[2], f, out[d + 2]);
+        out[d + 3] = __builtin_fmaf(x[3], f, out[d + 3]);
+      }
+    }
+    if (q_ok) {
+      const float inv = (L > 0.f) ? 1.f / L : 0.f;
+      float* orow = a.o + (q_base + qi) * D + hh * DH;
+#pragma unroll
+      for (int d = 0; d < DH; d += 4)
+        *(f32x4*)(orow + d) = f32x4{out[d] * inv, out[d + 1] * inv, out[d + 2] * inv, out[d + 3] * inv};
+      if (a.lse != nullptr && hh == 0) a.lse[q_base + qi] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
+    }
   }
 }
 
@@ -153,11 +208,11 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
   a.window = s.window;
   a.c2 = s.scale * kLog2e;
   a.n_qtiles = (s.Sq + kRows - 1) / kRows;
-  dim3 grid((unsigned)((int64_t)a.n_qtiles * s.B * s.Hq)), block(128);
+  dim3 grid((unsigned)((int64_t)a.n_qtiles * s.B * s.Hq));
   if (s.D == 128)
-    hipLaunchKernelGGL((fwd_f32_kernel<128>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_f32_kernel<128, 8>), grid, dim3(64 * 8), 0, stream, a);
   else
-    hipLaunchKernelGGL((fwd_f32_kernel<64>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_f32_kernel<64, 8>), grid, dim3(64 * 8), 0, stream, a);
   return hipGetLastError();
 }
 
