@@ -32,6 +32,10 @@
 //     [key][dim] tile.  P lines up with V because K rows sit in LDS with bits
 //     2 and 3 of the key index swapped inside each 32-key block, which makes
 //     the 8 keys a lane holds for each 16-key step consecutive.
+//   * a band (sliding window without a causal mask) is dispatched with a
+//     head's query tiles back to back, odd tiles walking their K/V tiles
+//     downwards, so two neighbouring query tiles read the K/V they share at
+//     about the same time and HBM delivers it once.
 //   * two or more wavefronts share each SIMD, so one wavefront's softmax
 //     overlaps another's matrix-core work.  Apart from the rare wave-uniform
 //     rescale, the only
@@ -115,8 +119,15 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     // Blocks are dispatched round-robin over the 8 XCDs; give each XCD a
     // contiguous set of heads so a head's K/V stays in one L2.
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    bh = xcd * a.xcd_heads + slot % a.xcd_heads;
-    rank = slot / a.xcd_heads;
+    if (a.window >= 0 && !a.causal) {
+      // a band: a head's query tiles back to back, so neighbouring tiles,
+      // which share K/V, run at the same time (see the tile order below)
+      bh = xcd * a.xcd_heads + slot / a.n_qtiles;
+      rank = slot % a.n_qtiles;
+    } else {
+      bh = xcd * a.xcd_heads + slot % a.xcd_heads;
+      rank = slot / a.xcd_heads;
+    }
   } else {
     bh = blockIdx.x % BH;
     rank = blockIdx.x / BH;
@@ -200,12 +211,12 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
   }
   const int nbw = (NB - wave + NW - 1) / NW;   // blocks this wavefront issues
   const uint32_t sK0 = lds_addr(sK), sV0 = lds_addr(sV);
-  auto issue = [&](int tile) {
+  auto issue = [&](int tile, int slot) {
     const int kt = tile * BN;
     const uint32_t bytes = (uint32_t)(min(BN, a.Sk - kt) * D * 2);
     const auto rk = make_rsrc(kh + (size_t)kt * D, bytes);
     const auto rv = make_rsrc(vh + (size_t)kt * D, bytes);
-    const uint32_t kdst = sK0 + (tile & 1) * KSLOT, vdst = sV0 + (tile & 1) * VSLOT;
+    const uint32_t kdst = sK0 + slot * KSLOT, vdst = sV0 + slot * VSLOT;
 #pragma unroll
     for (int i = 0; i < NBW - 1; ++i) dma16(disk[i] ? rk : rv, doff[i], (disk[i] ? kdst : vdst) + ddst[i]);
     if (NB % NW == 0 || nbw == NBW)
@@ -346,14 +357,24 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     }
   };
 
-  // K(t) and V(t) land in slot t&1; the loads of tile t+1 are issued as soon
-  // as every wavefront is done with tile t-1 (the barrier), so they fly while
-  // tile t is multiplied.
-  if (t_begin < t_end) issue(t_begin);
-  for (int tile = t_begin; tile < t_end; ++tile) {
+  // The K/V of step i land in slot i&1; the loads of step i+1 are issued as
+  // soon as every wavefront is done with step i-1 (the barrier), so they fly
+  // while step i is multiplied.
+  // A band (window, no causal mask): odd query tiles walk their K/V tiles
+  // downwards.  Query tiles r and r + 1 share their K/V tiles at the edge
+  // between them; with the alternating order both reach those tiles at the
+  // same step of their walk, one dispatch apart, so the second read finds
+  // them in L2 (HBM reads of the window-encoder shape: 402 MB -> 304 MB,
+  // the size of q, k and v).
+  const bool down = (w >= 0) && !a.causal && (qtile & 1);
+  const int n_t = t_end - t_begin;
+  auto tile_at = [&](int i) { return down ? t_end - 1 - i : t_begin + i; };
+  if (n_t > 0) issue(tile_at(0), 0);
+  for (int i = 0; i < n_t; ++i) {
+    const int tile = tile_at(i);
     wait_vmcnt<0>();
     __syncthreads();
-    if (tile + 1 < t_end) issue(tile + 1);
+    if (i + 1 < n_t) issue(tile_at(i + 1), (i + 1) & 1);
     // skip the matrix work of a tile no row of this wavefront can see
     const int kt0 = tile * BN, kt1 = kt0 + BN - 1;
     bool any = kt0 < a.Sk;
@@ -361,8 +382,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     if (w >= 0) any = any && (kt0 <= phi + w) && (kt1 >= plo - w);
     if (any) {
       f32x16 st[NKB];
-      qk(tile & 1, st);
-      softmax_pv(tile & 1, tile, st);
+      qk(i & 1, st);
+      softmax_pv(i & 1, tile, st);
     }
   }
 
