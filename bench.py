@@ -516,6 +516,13 @@ def run_only(name: str, steps: int, warmup: int, dev):
             def fn(i):
                 q, k, v, oo, ll = cp[i % 3]
                 ops.attn_fwd(q, k, v, causal=bool(w["causal"]), window=window, scale=w["scale"], out=oo, lse=ll)
+    elif name == "tiny_f32":
+        w = synth.workload_inputs(name, dev)
+        o = torch.empty_like(w["q"])
+        lse = torch.empty(w["B"], w["Hq"], w["Sq"], dtype=torch.float32, device=dev)
+
+        def fn(i):
+            ops.attn_fwd_f32(w["q"], w["k"], w["v"], causal=False, scale=w["scale"], out=o, lse=lse)
     elif name in ("gqa_decode", "long_decode"):
         w = synth.workload_inputs(name, dev)
         o = torch.empty_like(w["q"])
@@ -544,8 +551,8 @@ def main():
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--only", default=None,
                     help="time one workload alone and print its launch statistics (for profilers): "
-                         "causal_prefill, fp8_prefill, window_encoder, fp8_window_encoder, global_layer, "
-                         "backward, gqa_decode, long_decode")
+                         "tiny_f32, causal_prefill, fp8_prefill, window_encoder, fp8_window_encoder, "
+                         "global_layer, backward, gqa_decode, long_decode")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
