@@ -113,3 +113,24 @@ def test_backward_deterministic_and_delta():
         assert torch.equal(x, y)
     ref = (to_numpy_exact(do).astype(np.float64) * to_numpy_exact(o)).sum(axis=-1)
     np.testing.assert_allclose(to_numpy_exact(delta), ref, rtol=0, atol=1e-4)
+
+
+def test_backward_full_size_sampled_heads():
+    """The causal-prefill shape the bench times (B4 H16 S2048 D128, one launch
+    pair over all 64 heads); heads are independent (no GQA), so the fp64
+    gradient oracle of a head's own q, k, v, dout slice is exact for it."""
+    w = synth.WORKLOADS["causal_prefill"]
+    B, H, S, D = w["B"], w["Hq"], w["Sq"], w["D"]
+    q, k, v = synth.draw_qkv((B, H, S, D), (B, H, S, D), "bf16", synth.SEEDS["causal_prefill"], DEV)
+    do = synth.draw_grad((B, H, S, D), "bf16", synth.SEEDS["causal_prefill"], DEV)
+    scale = synth.default_scale(D)
+    announce(f"bwd full size B{B} H{H} S{S} D{D} causal, sampled heads")
+    o, lse = ops.attn_fwd(q, k, v, causal=True, scale=scale)
+    dq, dk, dv = ops.attn_bwd(q, k, v, o, do, lse, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (1, 7), (3, 15)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rq, rk, rv, _ = oracle.attention_backward(to_numpy_exact(q[sl]), to_numpy_exact(k[sl]),
+                                                  to_numpy_exact(v[sl]), to_numpy_exact(do[sl]), scale, True, -1)
+        for name, got, ref in (("dq", dq[sl], rq), ("dk", dk[sl], rk), ("dv", dv[sl], rv)):
+            _check(name, got, ref, f"full size b{b} h{h}")
