@@ -298,11 +298,13 @@ def test_runs_on_the_callers_stream():
 
 
 def test_graph_replay():
-    """The prefill, the fp8 prefill, the backward and the decode (caller
-    workspace) captured in one HIP graph: every replay, with eager work and
-    synchronisations between replays, gives the eager results bit for bit."""
+    """The prefill (bf16 and fp32), the fp8 prefill, the backward, the decode
+    (caller workspace) and the allocation-free decode captured in one HIP
+    graph: every replay, with eager work and synchronisations between
+    replays, gives the eager results bit for bit."""
     announce("graph capture and replay")
     q, k, v = synth.draw_qkv((2, 4, 333, 128), (2, 2, 333, 128), "bf16", 5, DEV)
+    qf, kf, vf = synth.draw_qkv((1, 2, 150, 64), (1, 1, 150, 64), "f32", 9, DEV)
     q8, k8, v8, qd, kd, vd = synth.draw_qkv_fp8((1, 4, 200, 64), (1, 4, 200, 64), 6, DEV)
     qd1, kd1, vd1 = synth.draw_qkv((4, 8, 128), (4, 2, 3000, 128), "bf16", 7, DEV)
     do = synth.draw_grad(q.shape, "bf16", 8, DEV)
@@ -313,7 +315,9 @@ def test_graph_replay():
                 lse8=torch.empty(1, 4, 200, device=DEV),
                 od=torch.empty_like(qd1), lsed=torch.empty(4, 8, device=DEV),
                 dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
-                delta=torch.empty(2, 4, 333, device=DEV))
+                delta=torch.empty(2, 4, 333, device=DEV),
+                of=torch.empty_like(qf), lsef=torch.empty(1, 2, 150, device=DEV),
+                on=torch.empty_like(qd1), lsen=torch.empty(4, 8, device=DEV))
 
     def work():
         ops.attn_fwd(q, k, v, causal=True, out=bufs["o"], lse=bufs["lse"])
@@ -321,6 +325,8 @@ def test_graph_replay():
         ops.attn_bwd(q, k, v, bufs["o"], do, bufs["lse"], causal=True, dq=bufs["dq"], dk=bufs["dk"],
                      dv=bufs["dv"], delta=bufs["delta"])
         ops.attn_decode_ex(qd1, kd1, vd1, ns, out=bufs["od"], lse=bufs["lsed"], workspace=ws)
+        ops.attn_fwd_f32(qf, kf, vf, causal=True, out=bufs["of"], lse=bufs["lsef"])
+        ops.attn_decode_noalloc(qd1, kd1, vd1, 21, bufs["on"], lse=bufs["lsen"])
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
