@@ -51,7 +51,11 @@ int check_fwd(const void* q, const void* k, const void* v, const void* o, int B,
     return ATTN_ERR_ARG;
   const int64_t bh = (int64_t)B * Hq;
   if (bh > INT32_MAX / 8) return ATTN_ERR_SHAPE;
-  if (((int64_t)Sq + 63) / 64 * bh > INT32_MAX) return ATTN_ERR_SHAPE;  // grid size
+  // bf16 / fp8 prefill (and the backward's dq pass): 256-row workgroups of
+  // 512 threads, or 128-row ones of 256
+  if (!ea::dispatch_fits(((int64_t)Sq + 255) / 256 * bh, 512) ||
+      !ea::dispatch_fits(((int64_t)Sq + 127) / 128 * bh, 256))
+    return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }
 
@@ -67,9 +71,11 @@ int check_decode(const void* q, const void* kc, const void* vc, const void* o, i
   if (Sk > 0 && (kc == nullptr || vc == nullptr)) return ATTN_ERR_NULL;
   if (misaligned(q, 16) || misaligned(kc, 16) || misaligned(vc, 16) || misaligned(o, 16))
     return ATTN_ERR_ARG;
+  // split kernel: one 256-thread workgroup per (chunk, kv head, batch row,
+  // group of 16 query heads); combine: one per (b, h, group of 256 partials)
   const int64_t nhg = ((Hq / Hkv) + 15) / 16;
-  if ((int64_t)num_splits * Hkv * B * nhg > INT32_MAX) return ATTN_ERR_SHAPE;
-  if (bh * ((int64_t)num_splits + 255) / 256 * (D / 64) > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (!ea::dispatch_fits((int64_t)num_splits * Hkv * B * nhg, 256)) return ATTN_ERR_SHAPE;
+  if (!ea::dispatch_fits(bh * (((int64_t)num_splits + 255) / 256), 256)) return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }
 
@@ -192,6 +198,8 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
   int st = check_fwd(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, window, scale);
   if (st != ATTN_OK || (int64_t)B * Hq * Sq == 0) return st;
   if (misaligned(lse, 4)) return ATTN_ERR_ARG;
+  if (!ea::dispatch_fits(((int64_t)Sq + ea::kF32Rows - 1) / ea::kF32Rows * B * Hq, ea::kF32Threads))
+    return ATTN_ERR_SHAPE;
   return to_status(ea::launch_fwd_f32(q, k, v, o, lse,
                                       fwd_shape(B, Hq, Hkv, Sq, Sk, D, causal, window, scale),
                                       stream));
@@ -228,7 +236,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if (misaligned(dout, 16) || misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16) ||
       misaligned(lse, 4) || misaligned(delta, 4))
     return ATTN_ERR_ARG;
-  if (((int64_t)Sk + 127) / 128 * B * Hkv > INT32_MAX) return ATTN_ERR_SHAPE;  // grid size
+  // dk/dv pass: 128-key workgroups of 256 threads
+  if (!ea::dispatch_fits(((int64_t)Sk + 127) / 128 * B * Hkv, 256)) return ATTN_ERR_SHAPE;
   return to_status(ea::launch_bwd((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                                   (const uint16_t*)o, (const uint16_t*)dout, lse, (uint16_t*)dq,
                                   (uint16_t*)dk, (uint16_t*)dv, delta,

@@ -33,8 +33,8 @@ struct F32Args {
   int n_qtiles;
 };
 
-constexpr int kRows = 16;  // query rows per workgroup (= lanes per quarter)
-constexpr int kNW = 16;    // wavefronts per workgroup
+constexpr int kRows = kF32Rows;       // query rows per workgroup (= lanes per quarter)
+constexpr int kNW = kF32Threads / 64;  // wavefronts per workgroup
 
 template <int D>
 __global__ __launch_bounds__(64 * kNW) void fwd_f32_kernel(F32Args a) {

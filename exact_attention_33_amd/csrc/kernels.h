@@ -8,6 +8,17 @@
 
 namespace ea {
 
+// A dispatch counts its work-items (grid blocks x block threads) in 32 bits;
+// the host checks each launch geometry against this before any launch.
+constexpr int64_t kMaxDispatchItems = 0xffffffffLL;
+inline bool dispatch_fits(int64_t blocks, int64_t threads) {
+  return blocks >= 0 && blocks <= kMaxDispatchItems / threads;
+}
+
+// fp32 prefill geometry: query rows and threads per workgroup.
+constexpr int kF32Rows = 16;
+constexpr int kF32Threads = 1024;
+
 struct FwdShape {
   int B, Hq, Hkv, Sq, Sk, D;
   int causal, window;

@@ -51,7 +51,8 @@ extern "C" {
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,      /* a required pointer is NULL                                  */
-  ATTN_ERR_SHAPE = 2,     /* a size is negative, or too large for the kernels' indexing  */
+  ATTN_ERR_SHAPE = 2,     /* a size is negative, or too large for the kernels' indexing
+                             or for one launch (grid blocks x threads must stay < 2^32) */
   ATTN_ERR_GQA = 3,       /* Hkv < 1 while Hq > 0, or Hq % Hkv != 0                      */
   ATTN_ERR_HEADDIM = 4,   /* D is not 64 or 128                                          */
   ATTN_ERR_SPLITS = 5,    /* num_splits < 1, or num_splits > max(Sk, 1)                  */

@@ -192,3 +192,19 @@ def test_noalloc_decode_validation(L):
     assert L.attn_decode_workspace_bytes(64, 32, 128, 64) > ops.NOALLOC_BYTES
     assert call(B=64, Hq=32, Hkv=8, Sk=1024, ns=64) == WORKSPACE
     assert L.attn_decode_workspace_bytes(16, 32, 128, 64) <= ops.NOALLOC_BYTES
+
+
+def test_launch_size_limits(L):
+    """A dispatch counts its work-items (blocks x threads) in 32 bits: shapes
+    whose grid would exceed that are refused on the host with ATTN_ERR_SHAPE,
+    before any launch."""
+    # bf16 / fp8 / fp32 prefill: 2^16 query tiles x 256 heads x 512 threads = 2^33
+    for f32 in (False, True):
+        assert fwd(L, B=1, Hq=256, Hkv=256, Sq=1 << 24, Sk=16, f32=f32) == SHAPE
+    # the fp32 kernel's 16-row, 1024-thread workgroups: 2^17 x 64 x 1024 = 2^33
+    assert fwd(L, B=1, Hq=64, Hkv=64, Sq=1 << 21, Sk=16, f32=True) == SHAPE
+    # decode split kernel: 2^20 chunks x 16 kv heads x 16 rows x 256 threads = 2^36
+    assert dec_ex(L, B=16, Hq=16, Hkv=16, Sk=1 << 20, D=128, ns=1 << 20) == SHAPE
+    # backward dk/dv pass: 2^21 key tiles x 8 kv heads x 256 threads = 2^32
+    assert L.attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                      1, 8, 8, 16, 1 << 28, 64, 0, -1, 0.125, None) == SHAPE
