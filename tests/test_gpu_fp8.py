@@ -115,6 +115,7 @@ def _rows_ref(host, desc, scale, causal, window, rows):
     (1, 1, 1, 33, 97, 0, -1),        # tiny, Sq != Sk
     (1, 2, 2, 1024, 1024, 1, -1),    # several full tiles
     (1, 2, 1, 600, 200, 1, -1),      # Sq > Sk causal: the first 400 rows see no key
+    (1, 8, 2, 256, 16384, 1, -1),    # a 256-row block against a 16384-key cache
 ], ids=lambda s: "B{}Hq{}Hkv{}Sq{}Sk{}c{}w{}".format(*s))
 def test_fp8_parity(shape):
     B, Hq, Hkv, Sq, Sk, causal, window = shape

@@ -105,6 +105,19 @@ def test_prefill_shapes(shape, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode", [(1, -1), (0, -1), (1, 700)], ids=["causal", "full", "causal_w700"])
+def test_chunked_prefill_long_cache(dtype, mode):
+    """A block of 256 new query rows against a 16384-key cache (Sq << Sk: row
+    i sees keys up to i + Sk - Sq, bottom-right causal alignment), GQA 4:1,
+    every row checked against the oracle: many K/V tiles per workgroup, the
+    causal diagonal at the far end of the key range."""
+    causal, window = mode
+    o, lse, o_ref, lse_ref = _prefill_case(1, 8, 2, 256, 16384, 128, causal, window, dtype, seed=21)
+    check_o(o, o_ref, dtype, f"chunked prefill {mode}")
+    check_lse(lse, lse_ref, dtype, f"chunked prefill {mode}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_prefill_peaky(dtype):
     """scale = 1 makes the softmax peaky, so |o| = O(1) and errors are not hidden."""
     for shape in [(2, 4, 2, 300, 300, 128, 1, -1), (1, 4, 4, 400, 400, 64, 0, 64)]:
