@@ -186,6 +186,8 @@ DECODE_SHAPES = [
     (1, 4, 1, 10, 128, 6),                # L = 2: chunk 5 empty
     (3, 32, 8, 4097, 128, 64),
     (1, 32, 1, 3000, 128, 16),            # 32 query heads per kv head: two head groups
+    (2, 40, 2, 3000, 128, 16),            # 20 per kv head: a full group of 16 and one of 4
+    (1, 6, 2, 999, 64, 5),                # 3 per kv head (odd), ragged chunks
     (1, 16, 16, 2048, 64, 1),
     (2, 8, 2, 3000, 128, 65),             # 65 partials: one wavefront's 64 leaves plus one
     (1, 8, 2, 5000, 64, 200),             # four combine wavefronts, the last with 8 leaves
