@@ -35,6 +35,7 @@ MUTANTS = {
     "exp sign": ("e = np.exp(s - m_safe[:, None])", "e = np.exp(m_safe[:, None] - s)"),
     "merge drops a factor": ("return M, l1 * f1 + l2 * f2,", "return M, l1 * f1 + l2,"),
     "merge max->min": ("M = np.maximum(m1, m2)", "M = np.minimum(m1, m2)"),
+    "chunk length floored": ("    L = -(-Sk // num_splits)\n", "    L = Sk // num_splits if Sk >= num_splits else 1\n"),
     "chunk bound off by one": ("min((c + 1) * L, Sk)) for c in range(num_splits)]",
                                "min((c + 1) * L - 1, Sk)) for c in range(num_splits)]"),
     "online alpha inverted": ("alpha = np.where(np.isfinite(m), np.exp(m - m_ref), 0.0)",
